@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for block-top-k sparse paged decode.
+
+TEST INFRASTRUCTURE: imported only by the test suite, the smoke check and the
+benchmark's CPU-baseline leg.  The GPU library never imports it.
+"""
+
+from .block_topk import *  # noqa: F401,F403
+from .block_topk import __all__  # noqa: F401
