@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of block-top-k sparse paged decode on one MI355X.
+
+One step = one decode query per request through one attention layer: the
+centroid update for the pages this step's token completes, the indexer
+(group-mean query, centroid scores through the page table, exact top-k with
+the reserved first / last pages), and split-K attention over the selected
+pages.  Steps cycle over several independent layers (separate KV pools and
+centroid tables of the same shape), so a step's working set is not still
+sitting in the 256 MB on-package cache from the previous visit.  The dense
+paged decode over every page is timed afterwards on the same layers, for the
+speedup.  All inputs are synthetic and seeded.
+
+Prints one JSON line on stdout.  Progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MALL_BYTES = 256 << 20           # on-package cache the layer rotation has to defeat
+METRIC = "sparse decode queries/s + achieved HBM GB/s (% peak) + speedup vs dense paged"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- bytes
+def _pages(L, S):
+    return -(-int(L) // S)
+
+
+def indexer_bytes(w, L):
+    """Bytes the indexer must move for one request of length L: candidate
+    centroid rows, page-table entries, the query and the selection."""
+    n_b = _pages(L, w.page_size)
+    n_c = max(n_b - w.n_bos - w.n_eos, 0)
+    e = w.elem_bytes
+    return (n_c * w.num_kv_heads * w.head_dim_qk * e + 4 * n_b
+            + w.num_q_heads * w.head_dim_qk * e + 4 * w.num_kv_heads * w.k_tot)
+
+
+def attention_bytes(w, L, dense=False):
+    """Bytes attention must move for one request: K/V of the attended
+    tokens (MLA reads each 576-dim row once), q, o, and the selection and
+    page-table entries it walks."""
+    S, e = w.page_size, w.elem_bytes
+    n_b = _pages(L, S)
+    row = w.head_dim_qk * e if w.v_aliases_k else (w.head_dim_qk + w.head_dim_v) * e
+    qo = w.num_q_heads * (w.head_dim_qk + w.head_dim_v) * e
+    if dense:
+        return int(L) * w.num_kv_heads * row + 4 * n_b + qo
+    pages = min(n_b, w.k_tot)
+    tokens = min(pages * S, int(L))
+    return tokens * w.num_kv_heads * row + qo + 8 * w.num_kv_heads * pages
+
+
+def centroid_bytes(w, n_pages):
+    e = w.elem_bytes
+    return n_pages * (w.num_kv_heads * w.head_dim_qk * e * (w.page_size + 1) + 4)
+
+
+# ---------------------------------------------------------------- cpu baseline
+def cpu_baseline(w, lay, layer, seconds, max_requests):
+    """The fp64 oracle's sparse step, timed on the host on a sample of
+    requests of layer 0 (single BLAS thread)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle as orc
+    import synth
+
+    L = synth.step_seq_lens(lay, 0)
+    reqs = list(range(min(w.batch, max_requests)))
+    data = []
+    for b in reqs:
+        n = _pages(L[b], w.page_size)
+        idx = layer["pt"][b, :n].long()
+        k = layer["K"][idx].float().cpu().numpy()
+        v = None if layer["V"] is None else layer["V"][idx].float().cpu().numpy()
+        q = layer["q"][b].float().cpu().numpy()
+        data.append((b, k, v, q))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        cents = [orc.request_centroids(k, int(L[b]) - (1 if L[b] % w.page_size == 0 else 0),
+                                       w.dtype) for b, k, v, q in data]
+        setup_s = time.perf_counter() - t0
+        vd = w.head_dim_v if w.v_aliases_k else None
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            for (b, k, v, q), cent in zip(data, cents):
+                Lb = int(L[b])
+                if Lb % w.page_size == 0:          # the page this token completes
+                    p = Lb // w.page_size - 1
+                    cent[p] = orc.page_centroids(k[p:p + 1], w.dtype)[0]
+                orc.sparse_decode_request(q, k, v, cent, Lb, w.sm_scale, w.topk, w.n_bos,
+                                          w.n_eos, v_dims=vd)
+                done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {
+        "value": done / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{len(reqs)} of {w.batch} requests of layer 0, {done // len(reqs)} passes "
+                   f"({done} sparse decode queries: completed-page centroid, group-mean query, "
+                   f"centroid scores, exact top-k, attention over the selected pages), "
+                   f"fp64 numpy on one BLAS thread, {el:.1f} s"),
+        "setup_centroids_s": setup_s,
+    }
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="qwen3_0p6b_b32_l32k")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="distinct KV pools cycled over (0: enough to defeat the 256 MB cache)")
+    ap.add_argument("--dense-steps", type=int, default=40)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library "
+              f"has no multi-GPU path: each GPU would run its own shard independently)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import block_sparse_paged_amd as vx
+    import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    vx.load_library()
+    w = synth.get_workload(args.workload)
+    lay = synth.build_layout(w)
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: {w.description}")
+
+    T = w.steps
+    L_steps = [synth.step_seq_lens(lay, s) for s in range(T)]
+    step_bytes = [sum(indexer_bytes(w, L) + attention_bytes(w, L) for L in Ls)
+                  + centroid_bytes(w, len(synth.completed_pages(lay, s)))
+                  for s, Ls in enumerate(L_steps)]
+    mean_step_bytes = float(np.mean(step_bytes))
+    pool_bytes = lay.num_pages * w.num_kv_heads * w.page_size * w.elem_bytes * (
+        w.head_dim_qk + (0 if w.v_aliases_k else w.head_dim_v))
+    n_layers = args.layers or max(2, math.ceil(3 * MALL_BYTES / mean_step_bytes) + 1)
+    n_layers = max(1, min(n_layers, int((48 << 30) // max(pool_bytes, 1))))
+    log(f"step bytes {mean_step_bytes / 1e6:.1f} MB, pool {pool_bytes / 1e9:.2f} GB, "
+        f"{n_layers} layers")
+
+    pt = torch.from_numpy(lay.page_table).to(dev)
+    max_len = int(lay.seq_lens0.max()) + T - 1
+    seq_dev = [torch.from_numpy(L.astype(np.int32)).to(dev) for L in L_steps]
+    batches = [vx.Batch(page_table=pt, seq_lens=s, num_q_heads=w.num_q_heads, max_seq_len=max_len)
+               for s in seq_dev]
+    done_ids = [torch.from_numpy(synth.completed_pages(lay, s)).to(dev) for s in range(T)]
+    setup_ids = torch.from_numpy(synth.setup_full_pages(lay)).to(dev)
+
+    layers = []
+    for i in range(n_layers):
+        wl = w.with_(seed=w.seed + 7919 * i)
+        K, V = synth.make_kv_pool(wl, lay, device=dev)
+        cent = torch.zeros((lay.num_pages, w.num_kv_heads, w.head_dim_qk), dtype=w.torch_dtype,
+                           device=dev)
+        kv = vx.PagedKV(k_cache=K, v_cache=V, centroids=cent, head_dim_v=w.head_dim_v)
+        vx.centroid_update(kv, setup_ids)              # cache construction (setup)
+        qs = [synth.make_queries(wl, lay, s).to(dev) for s in range(T)]
+        layers.append({"K": K, "V": V, "kv": kv, "q": qs[0], "qs": qs, "pt": pt})
+        log(f"layer {i} ready")
+    torch.cuda.synchronize()
+
+    sel = torch.empty((w.batch, w.num_kv_heads, w.k_tot), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    kv0 = layers[0]["kv"]
+    ws_idx = vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, kv0, batches[0])
+    ws_dec = vx.alloc_workspace(vx.VX_OP_SPARSE_DECODE, kv0, batches[0], w.k_tot)
+    ws_full = vx.alloc_workspace(vx.VX_OP_FULL_DECODE, kv0, batches[0])
+    stream = torch.cuda.current_stream()
+
+    # prepared calls per (layer, step-of-schedule)
+    calls = []
+    for li, lay_i in enumerate(layers):
+        per = []
+        for s in range(T):
+            kv, bt, q = lay_i["kv"], batches[s], lay_i["qs"][s]
+            c_upd = (vx.prepare_centroid_update(kv, done_ids[s], stream)
+                     if done_ids[s].numel() else None)
+            c_idx = vx.prepare_score_topk(kv, bt, q, w.topk, w.n_bos, w.n_eos, sel, ws_idx, stream)
+            c_dec = vx.prepare_sparse_paged_decode(kv, bt, q, sel, w.sm_scale, out, lse, ws_dec,
+                                                   stream)
+            c_full = vx.prepare_full_paged_decode(kv, bt, q, w.sm_scale, out, lse, ws_full, stream)
+            per.append((c_upd, c_idx, c_dec, c_full))
+        calls.append(per)
+
+    K_steps, W_steps = args.steps, args.warmup
+    nL = n_layers
+
+    def schedule(i):
+        return calls[i % nL][i % T]
+
+    # ---------------- sparse steps
+    for i in range(W_steps):
+        c_upd, c_idx, c_dec, _ = schedule(i)
+        if c_upd:
+            c_upd()
+        c_idx()
+        c_dec()
+    torch.cuda.synchronize()
+    log(f"warmup {W_steps} steps done")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        c_upd, c_idx, c_dec, _ = schedule(W_steps + i)
+        e = ev[i]
+        e[0].record(stream)
+        if c_upd:
+            c_upd()
+        e[1].record(stream)
+        c_idx()
+        e[2].record(stream)
+        c_dec()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {K_steps} sparse steps: {wall * 1e3:.2f} ms")
+
+    seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    ms_per_step = wall * 1e3 / K_steps
+    qps = w.batch * K_steps / wall
+
+    # per-call algorithmic bytes, averaged over the steps run
+    sched = [(W_steps + i) % T for i in range(K_steps)]
+    b_upd = np.mean([centroid_bytes(w, len(synth.completed_pages(lay, s))) for s in sched])
+    b_idx = np.mean([sum(indexer_bytes(w, L) for L in L_steps[s]) for s in sched])
+    b_dec = np.mean([sum(attention_bytes(w, L) for L in L_steps[s]) for s in sched])
+    units = {
+        "centroid_update": (b_upd, float(seg[:, 0].mean())),
+        "score_topk": (b_idx, float(seg[:, 1].mean())),
+        "sparse_paged_decode": (b_dec, float(seg[:, 2].mean())),
+    }
+    kernels = {k: {"bytes_per_call": int(bb), "avg_ms": ms,
+                   "gbps": (bb / (ms * 1e-3) / 1e9) if ms > 0 else None}
+               for k, (bb, ms) in units.items()}
+    dom = max(units, key=lambda k: units[k][1])
+    bb, ms = units[dom]
+    achieved = bb / (ms * 1e-3) / 1e9
+    step_gbps = (b_upd + b_idx + b_dec) / (ms_per_step * 1e-3) / 1e9
+
+    # ---------------- dense comparator
+    dense = None
+    if not args.no_dense:
+        nd = args.dense_steps
+        for i in range(min(4, nd)):
+            schedule(i)[3]()
+        torch.cuda.synchronize()
+        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nd)]
+        t1 = time.perf_counter()
+        for i in range(nd):
+            evd[i][0].record(stream)
+            schedule(W_steps + i)[3]()
+            evd[i][1].record(stream)
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t1
+        dms = np.array([e[0].elapsed_time(e[1]) for e in evd])
+        dbytes = np.mean([sum(attention_bytes(w, L, dense=True) for L in L_steps[(W_steps + i) % T])
+                          for i in range(nd)])
+        dense = {"queries_per_s": w.batch * nd / dwall, "ms_per_step": dwall * 1e3 / nd,
+                 "avg_kernel_ms": float(dms.mean()), "bytes_per_step": int(dbytes),
+                 "gbps": dbytes / (dms.mean() * 1e-3) / 1e9,
+                 "pct_peak": 100.0 * dbytes / (dms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        log(f"dense: {dense['ms_per_step']:.3f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        layers[0]["q"] = layers[0]["qs"][0]
+        cpu = cpu_baseline(w, lay, layers[0], args.cpu_seconds, args.cpu_requests)
+
+    line = {
+        "metric": METRIC,
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": W_steps,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": int(max_len),
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
+                   "page_size": w.page_size, "topk": w.topk, "n_bos": w.n_bos,
+                   "n_eos": w.n_eos, "layers_cycled": n_layers},
+        "achieved_gbps": step_gbps,
+        "pct_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
+        "speedup_vs_dense": (dense["ms_per_step"] / ms_per_step) if dense else None,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "step_ms_p10_p50_p90": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
+        "algorithmic_bytes_per_step": int(b_upd + b_idx + b_dec),
+        "kernels": kernels,
+        "dense": dense,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

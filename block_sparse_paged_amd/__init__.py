@@ -1,0 +1,289 @@
+"""Python binding of libvx, the MI355X (gfx950) block-top-k sparse paged
+decode library.
+
+Argument marshalling only: every step of the method runs in the HIP kernels
+behind the C ABI declared in include/vx.h.  Tensors are passed as raw device
+pointers together with the current torch stream; nothing here computes on
+their contents.  The library must have been built in-tree
+(``python -m block_sparse_paged_amd.build``); without it, importing the
+compute entry points raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvx.so")
+
+VX_OK = 0
+VX_ERR_INVALID_ARGUMENT = 1
+VX_ERR_UNSUPPORTED = 2
+VX_ERR_WORKSPACE_TOO_SMALL = 3
+VX_ERR_HIP = 4
+
+VX_F32, VX_BF16 = 0, 1
+VX_OP_SCORE_TOPK, VX_OP_SPARSE_DECODE, VX_OP_FULL_DECODE = 0, 1, 2
+
+# Symbols include/vx.h declares (checked by the ABI tests).
+EXPORTS = ("vx_centroid_update", "vx_score_topk", "vx_sparse_paged_decode",
+           "vx_full_paged_decode", "vx_workspace_size", "vx_set_pages_per_split",
+           "vx_status_string", "vx_version")
+
+
+class VxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class PagedKVStruct(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("v_aliases_k", ctypes.c_int32), ("reserved_", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("centroids", ctypes.c_void_p),
+    ]
+
+
+class BatchStruct(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("max_pages_per_req", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libvx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_sparse_paged_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, F32, VP = (ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t,
+                           ctypes.c_float, ctypes.c_void_p)
+    kvp, btp = P(PagedKVStruct), P(BatchStruct)
+    lib.vx_centroid_update.argtypes = [kvp, VP, I32, VP]
+    lib.vx_score_topk.argtypes = [kvp, btp, VP, I32, I32, I32, VP, VP, SZ, VP]
+    lib.vx_sparse_paged_decode.argtypes = [kvp, btp, VP, VP, I32, F32, VP, VP, VP, SZ, VP]
+    lib.vx_full_paged_decode.argtypes = [kvp, btp, VP, F32, VP, VP, VP, SZ, VP]
+    lib.vx_workspace_size.argtypes = [I32, kvp, btp, I32, P(SZ)]
+    lib.vx_set_pages_per_split.argtypes = [I32]
+    lib.vx_status_string.argtypes = [I32]
+    lib.vx_status_string.restype = ctypes.c_char_p
+    lib.vx_version.argtypes = []
+    for name in ("vx_centroid_update", "vx_score_topk", "vx_sparse_paged_decode",
+                 "vx_full_paged_decode", "vx_workspace_size", "vx_set_pages_per_split",
+                 "vx_version"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().vx_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != VX_OK:
+        raise VxError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_DT = {torch.float32: VX_F32, torch.bfloat16: VX_BF16}
+
+
+@dataclass
+class PagedKV:
+    """The caller-owned paged KV cache and centroid table (device tensors)."""
+    k_cache: torch.Tensor                  # [P, H_kv, S_p, D_qk]
+    v_cache: Optional[torch.Tensor]        # [P, H_kv, S_p, D_v] or None (V = K[..., :D_v])
+    centroids: torch.Tensor                # [P, H_kv, D_qk]
+    head_dim_v: Optional[int] = None
+
+    def struct(self) -> PagedKVStruct:
+        k = self.k_cache
+        P, H, S, D = k.shape
+        dv = self.v_cache.shape[-1] if self.v_cache is not None else (self.head_dim_v or D)
+        return PagedKVStruct(
+            dtype=_DT.get(k.dtype, -1), num_pages=P, page_size=S, num_kv_heads=H,
+            head_dim_qk=D, head_dim_v=dv, v_aliases_k=1 if self.v_cache is None else 0,
+            reserved_=0, k_cache=k.data_ptr(),
+            v_cache=None if self.v_cache is None else self.v_cache.data_ptr(),
+            centroids=self.centroids.data_ptr())
+
+
+@dataclass
+class Batch:
+    """Decode-batch metadata: page table and sequence lengths (device int32)."""
+    page_table: torch.Tensor               # [B, max_pages] int32
+    seq_lens: torch.Tensor                 # [B] int32
+    num_q_heads: int
+    max_seq_len: int                       # host-side bound used for planning
+
+    def struct(self) -> BatchStruct:
+        B, mp = self.page_table.shape
+        return BatchStruct(batch=B, num_q_heads=self.num_q_heads, max_pages_per_req=mp,
+                           max_seq_len=int(self.max_seq_len),
+                           page_table=self.page_table.data_ptr(),
+                           seq_lens=self.seq_lens.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def workspace_size(op: int, kv: PagedKV, batch: Batch, k_tot: int = 0) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    kvs, bs = kv.struct(), batch.struct()
+    _check(lib.vx_workspace_size(op, ctypes.byref(kvs), ctypes.byref(bs), k_tot,
+                                 ctypes.byref(out)), "vx_workspace_size")
+    return int(out.value)
+
+
+def alloc_workspace(op: int, kv: PagedKV, batch: Batch, k_tot: int = 0) -> torch.Tensor:
+    n = workspace_size(op, kv, batch, k_tot)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=kv.k_cache.device)
+
+
+def centroid_update(kv: PagedKV, page_ids: torch.Tensor, stream=None):
+    """vx_centroid_update: centroids of the listed (full) physical pages."""
+    _need(page_ids, "page_ids", torch.int32)
+    kvs = kv.struct()
+    _check(load_library().vx_centroid_update(ctypes.byref(kvs), _ptr(page_ids),
+                                             page_ids.numel(), _stream(stream)),
+           "vx_centroid_update")
+
+
+def score_topk(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
+               n_eos: int, sel: torch.Tensor, workspace: torch.Tensor, stream=None):
+    """vx_score_topk: selected logical pages per (request, KV head) into sel."""
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_score_topk(
+        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, _ptr(sel),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "vx_score_topk")
+
+
+def sparse_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sel: torch.Tensor,
+                        sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                        workspace: torch.Tensor, stream=None):
+    """vx_sparse_paged_decode: attention over the pages listed in sel."""
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    _need(out, "out")
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_sparse_paged_decode(
+        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), _ptr(sel), sel.shape[-1],
+        float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream(stream)), "vx_sparse_paged_decode")
+
+
+def full_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sm_scale: float,
+                      out: torch.Tensor, lse: Optional[torch.Tensor],
+                      workspace: torch.Tensor, stream=None):
+    """vx_full_paged_decode: attention over every page (the dense baseline)."""
+    _need(q, "q")
+    _need(out, "out")
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_full_paged_decode(
+        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), float(sm_scale), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "vx_full_paged_decode")
+
+
+def set_pages_per_split(n: int):
+    """Test hook: force the decode split size (0 = planner)."""
+    _check(load_library().vx_set_pages_per_split(int(n)), "vx_set_pages_per_split")
+
+
+def version() -> int:
+    return int(load_library().vx_version())
+
+
+class PreparedCall:
+    """A libvx call with its arguments marshalled once; calling it only
+    crosses the C ABI.  Holds references to every struct and tensor it
+    points at."""
+
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, fn, args, name, keep):
+        self._fn, self._args, self._name, self._keep = fn, args, name, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != VX_OK:
+            raise VxError(st, self._name)
+
+
+def prepare_centroid_update(kv: PagedKV, page_ids: torch.Tensor, stream=None) -> PreparedCall:
+    _need(page_ids, "page_ids", torch.int32)
+    kvs = kv.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), _ptr(page_ids), page_ids.numel(), _stream(stream))
+    return PreparedCall(lib.vx_centroid_update, args, "vx_centroid_update", (kvs, kv, page_ids))
+
+
+def prepare_score_topk(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, sel, workspace,
+                       stream=None) -> PreparedCall:
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, _ptr(sel),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall(lib.vx_score_topk, args, "vx_score_topk",
+                        (kvs, bs, kv, batch, q, sel, workspace))
+
+
+def prepare_sparse_paged_decode(kv: PagedKV, batch: Batch, q, sel, sm_scale, out, lse,
+                                workspace, stream=None) -> PreparedCall:
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    _need(out, "out")
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), _ptr(sel), sel.shape[-1],
+            float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    return PreparedCall(lib.vx_sparse_paged_decode, args, "vx_sparse_paged_decode",
+                        (kvs, bs, kv, batch, q, sel, out, lse, workspace))
+
+
+def prepare_full_paged_decode(kv: PagedKV, batch: Batch, q, sm_scale, out, lse, workspace,
+                              stream=None) -> PreparedCall:
+    _need(q, "q")
+    _need(out, "out")
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), float(sm_scale), _ptr(out),
+            _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall(lib.vx_full_paged_decode, args, "vx_full_paged_decode",
+                        (kvs, bs, kv, batch, q, out, lse, workspace))

@@ -1,0 +1,349 @@
+// C-ABI entry points of libvx: argument validation (before any HIP call),
+// launch planning, workspace layout and kernel dispatch.
+//
+// Planning ("workload planner for balanced GPU scheduling", Vortex article,
+// "A dual-stage programmable abstraction") is a pure function of the shapes:
+// every (request, KV head) is cut into splits of whole pages so that the
+// launch holds enough waves to keep all 256 CUs of an MI355X streaming, and
+// the fp32 partials the splits produce stay a small fraction of the K/V
+// bytes they replace.  Splits that fall beyond a short request's pages exit
+// at once, which keeps heterogeneous batches balanced without a device-side
+// work list.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/vx.h"
+#include "vx_internal.h"
+
+namespace {
+
+using namespace vx;
+
+constexpr int kNumCUs = 256;                    // MI355X
+constexpr int kSparseTargetWaves = kNumCUs * 8;
+constexpr int kFullTargetWaves = kNumCUs * 32;
+constexpr int kMlaTargetBlocks = kNumCUs * 2;
+constexpr int kMaxSplits = 1024;
+constexpr int kMaxCandidates = 16384;
+constexpr size_t kAlign = 256;
+constexpr bool kMlaAvailable = false;   // the MLA decode kernel is not built yet
+
+int g_pages_per_split_override = 0;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+int elem_bytes(int dtype) { return dtype == VX_F32 ? 4 : 2; }
+
+bool is_mla(const vx_paged_kv* kv) { return kv->head_dim_qk == 576; }
+
+vx_status check_kv(const vx_paged_kv* kv) {
+  if (!kv) return VX_ERR_INVALID_ARGUMENT;
+  if (kv->dtype != VX_F32 && kv->dtype != VX_BF16) return VX_ERR_INVALID_ARGUMENT;
+  if (kv->num_pages < 1 || kv->page_size < 1 || kv->num_kv_heads < 1 ||
+      kv->head_dim_qk < 1 || kv->head_dim_v < 1 || kv->reserved_ != 0)
+    return VX_ERR_INVALID_ARGUMENT;
+  if (kv->v_aliases_k != 0 && kv->v_aliases_k != 1) return VX_ERR_INVALID_ARGUMENT;
+  if (kv->v_aliases_k) {
+    if (kv->v_cache != nullptr || kv->head_dim_v > kv->head_dim_qk) return VX_ERR_INVALID_ARGUMENT;
+  }
+  if (kv->page_size != 16 && kv->page_size != 64) return VX_ERR_UNSUPPORTED;
+  const int dq = kv->head_dim_qk, dv = kv->head_dim_v;
+  if (dq == 576) {
+    if (!kMlaAvailable) return VX_ERR_UNSUPPORTED;
+    if (kv->dtype != VX_BF16 || dv != 512 || !kv->v_aliases_k || kv->num_kv_heads != 1 ||
+        kv->page_size != 64)
+      return VX_ERR_UNSUPPORTED;
+  } else if (dq == 64 || dq == 128) {
+    if (dv != dq) return VX_ERR_UNSUPPORTED;
+  } else {
+    return VX_ERR_UNSUPPORTED;
+  }
+  return VX_OK;
+}
+
+vx_status check_batch(const vx_paged_kv* kv, const vx_batch* bt) {
+  if (!bt) return VX_ERR_INVALID_ARGUMENT;
+  if (bt->batch < 0 || bt->num_q_heads < 1 || bt->max_pages_per_req < 1 || bt->max_seq_len < 1)
+    return VX_ERR_INVALID_ARGUMENT;
+  if (bt->num_q_heads % kv->num_kv_heads != 0) return VX_ERR_INVALID_ARGUMENT;
+  if ((long long)bt->max_pages_per_req * kv->page_size < bt->max_seq_len)
+    return VX_ERR_INVALID_ARGUMENT;
+  const int G = bt->num_q_heads / kv->num_kv_heads;
+  if (is_mla(kv)) {
+    if (G > 32) return VX_ERR_UNSUPPORTED;
+  } else if (G != 1 && G != 2 && G != 4 && G != 8) {
+    return VX_ERR_UNSUPPORTED;
+  }
+  return VX_OK;
+}
+
+int max_pages_eff(const vx_paged_kv* kv, const vx_batch* bt) {
+  return ceil_div(bt->max_seq_len, kv->page_size);
+}
+
+struct DecodePlan {
+  int pages_per_split = 1;
+  int n_split = 1;
+  size_t part_o_bytes = 0, part_ml_bytes = 0;
+  size_t ws_bytes() const { return part_o_bytes + part_ml_bytes; }
+};
+
+// Splits for `pages` pages per (request, KV head).
+DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, bool sparse) {
+  DecodePlan p;
+  const long long units = std::max(1LL, (long long)bt->batch * kv->num_kv_heads);
+  const int G = bt->num_q_heads / kv->num_kv_heads;
+  pages = std::max(pages, 1);
+  int pps;
+  if (g_pages_per_split_override > 0) {
+    pps = g_pages_per_split_override;
+  } else if (is_mla(kv)) {
+    const int n_want = std::max(1, ceil_div(kMlaTargetBlocks, units));
+    pps = ceil_div(pages, n_want);
+    // partials: G rows of (D_v + 2) fp32, written and read once per split
+    const double kv_bytes = (double)pages * kv->page_size * kv->head_dim_qk * 2;
+    while (ceil_div(pages, pps) > 1 &&
+           (double)ceil_div(pages, pps) * G * (kv->head_dim_v + 2) * 8 > 0.25 * kv_bytes)
+      ++pps;
+  } else {
+    const int target = sparse ? kSparseTargetWaves : kFullTargetWaves;
+    const int n_want = std::max(1, ceil_div(target, units));
+    pps = ceil_div(pages, n_want);
+    if (!sparse) pps = std::max(pps, 16);
+    const double kv_bytes = (double)pages * kv->page_size *
+                            (kv->head_dim_qk + kv->head_dim_v) * elem_bytes(kv->dtype);
+    while (ceil_div(pages, pps) > 1 &&
+           (double)ceil_div(pages, pps) * G * (kv->head_dim_v + 2) * 8 > 0.15 * kv_bytes)
+      ++pps;
+  }
+  pps = std::max(pps, ceil_div(pages, kMaxSplits));
+  p.pages_per_split = pps;
+  p.n_split = ceil_div(pages, pps);
+  if (p.n_split > 1) {
+    const size_t rows = (size_t)bt->batch * bt->num_q_heads * p.n_split;
+    p.part_o_bytes = align_up(rows * kv->head_dim_v * sizeof(float));
+    p.part_ml_bytes = align_up(rows * 2 * sizeof(float));
+  }
+  return p;
+}
+
+size_t score_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt) {
+  return align_up((size_t)bt->batch * kv->num_kv_heads * max_pages_eff(kv, bt) * sizeof(float));
+}
+
+vx_status hip_status(hipError_t e) { return e == hipSuccess ? VX_OK : VX_ERR_HIP; }
+
+vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
+                     const int32_t* sel, int32_t k_tot, float sm_scale, void* out, float* lse,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  const bool sparse = sel != nullptr;
+  const DecodePlan p = plan_decode(kv, bt, sparse ? k_tot : max_pages_eff(kv, bt), sparse);
+  if (ws_bytes < p.ws_bytes()) return VX_ERR_WORKSPACE_TOO_SMALL;
+  if (p.ws_bytes() > 0 && ws == nullptr) return VX_ERR_INVALID_ARGUMENT;
+  if (bt->batch == 0) return VX_OK;
+
+  DecodeArgs a{};
+  a.q = q;
+  a.k = kv->k_cache;
+  a.v = kv->v_aliases_k ? kv->k_cache : kv->v_cache;
+  a.pt = bt->page_table;
+  a.seq_lens = bt->seq_lens;
+  a.sel = sel;
+  a.B = bt->batch;
+  a.H_q = bt->num_q_heads;
+  a.H_kv = kv->num_kv_heads;
+  a.S_p = kv->page_size;
+  a.pt_stride = bt->max_pages_per_req;
+  a.k_tot = k_tot;
+  a.max_tokens = bt->max_seq_len;   // validated <= max_pages_per_req * page_size
+  a.pages_per_split = p.pages_per_split;
+  a.n_split = p.n_split;
+  a.v_stride_tok = kv->v_aliases_k ? kv->head_dim_qk : kv->head_dim_v;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  if (p.n_split > 1) {
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_o_bytes);
+  }
+  const int G = bt->num_q_heads / kv->num_kv_heads;
+  hipError_t e = is_mla(kv) ? launch_decode_mla(a, stream)
+                            : launch_decode_valu(kv->dtype, kv->head_dim_qk, G, a, stream);
+  if (e != hipSuccess) return VX_ERR_HIP;
+  if (p.n_split > 1) {
+    CombineArgs c{};
+    c.part_o = a.part_o;
+    c.part_ml = a.part_ml;
+    c.out = out;
+    c.lse = lse;
+    c.B = bt->batch;
+    c.H_q = bt->num_q_heads;
+    c.n_split = p.n_split;
+    c.D_v = kv->head_dim_v;
+    e = launch_combine(kv->dtype, c, stream);
+  }
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+vx_status vx_centroid_update(const vx_paged_kv* kv, const int32_t* page_ids, int32_t n_ids,
+                             hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if (n_ids < 0) return VX_ERR_INVALID_ARGUMENT;
+  if (n_ids == 0) return VX_OK;
+  if (!page_ids || !kv->k_cache || !kv->centroids) return VX_ERR_INVALID_ARGUMENT;
+  CentroidArgs a{};
+  a.k = kv->k_cache;
+  a.cent = kv->centroids;
+  a.ids = page_ids;
+  a.n_ids = n_ids;
+  a.H_kv = kv->num_kv_heads;
+  a.S_p = kv->page_size;
+  a.D = kv->head_dim_qk;
+  return hip_status(launch_centroid(kv->dtype, a, stream));
+}
+
+vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                        int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (topk < 0 || n_bos < 0 || n_eos < 1) return VX_ERR_INVALID_ARGUMENT;
+  if ((long long)topk + n_bos + n_eos > 0x7fffffffLL) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !sel || !kv->centroids || !batch->page_table || !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  const int mp = max_pages_eff(kv, batch);
+  if (mp > kMaxCandidates) return VX_ERR_UNSUPPORTED;
+  const size_t need = score_ws_bytes(kv, batch);
+  if (workspace_bytes < need) return VX_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return VX_ERR_INVALID_ARGUMENT;
+  const int k_tot = topk + n_bos + n_eos;
+  // device-side lengths are clamped to this bound, which keeps every page
+  // table read and score write in range even for out-of-contract lengths
+  const int max_tokens = batch->max_seq_len;
+  float* scores = reinterpret_cast<float*>(workspace);
+  const int max_cand = std::max(mp - n_bos - n_eos, 0);
+
+  const bool need_scores = max_cand > topk && topk > 0;   // else all or none are taken
+  if (need_scores) {
+    ScoreArgs s{};
+    s.q = q;
+    s.cent = kv->centroids;
+    s.pt = batch->page_table;
+    s.seq_lens = batch->seq_lens;
+    s.scores = scores;
+    s.B = batch->batch;
+    s.H_q = batch->num_q_heads;
+    s.H_kv = kv->num_kv_heads;
+    s.D = kv->head_dim_qk;
+    s.S_p = kv->page_size;
+    s.pt_stride = batch->max_pages_per_req;
+    s.score_stride = mp;
+    s.max_tokens = max_tokens;
+    s.n_bos = n_bos;
+    s.n_eos = n_eos;
+    const long long total = (long long)batch->batch * max_cand;
+    int cpb = ceil_div(total, 1024);
+    cpb = std::min(std::max(cpb, 16), 256);
+    s.cand_per_block = cpb;
+    hipError_t e = launch_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
+    if (e != hipSuccess) return VX_ERR_HIP;
+  }
+  TopkArgs t{};
+  t.scores = scores;
+  t.seq_lens = batch->seq_lens;
+  t.sel = sel;
+  t.B = batch->batch;
+  t.H_kv = kv->num_kv_heads;
+  t.S_p = kv->page_size;
+  t.score_stride = mp;
+  t.max_tokens = max_tokens;
+  t.topk = topk;
+  t.n_bos = n_bos;
+  t.n_eos = n_eos;
+  t.k_tot = k_tot;
+  return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
+}
+
+vx_status vx_sparse_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                                 const int32_t* sel, int32_t k_tot, float sm_scale, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (k_tot < 1) return VX_ERR_INVALID_ARGUMENT;
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !sel || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) ||
+      !batch->page_table || !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  return run_decode(kv, batch, q, sel, k_tot, sm_scale, out, lse, workspace, workspace_bytes,
+                    stream);
+}
+
+vx_status vx_full_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                               float sm_scale, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) || !batch->page_table ||
+      !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  return run_decode(kv, batch, q, nullptr, 0, sm_scale, out, lse, workspace, workspace_bytes,
+                    stream);
+}
+
+vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* batch,
+                            int32_t k_tot, size_t* bytes) {
+  if (!bytes) return VX_ERR_INVALID_ARGUMENT;
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  switch (op) {
+    case VX_OP_SCORE_TOPK:
+      if (max_pages_eff(kv, batch) > kMaxCandidates) return VX_ERR_UNSUPPORTED;
+      *bytes = score_ws_bytes(kv, batch);
+      return VX_OK;
+    case VX_OP_SPARSE_DECODE:
+      if (k_tot < 1) return VX_ERR_INVALID_ARGUMENT;
+      *bytes = plan_decode(kv, batch, k_tot, true).ws_bytes();
+      return VX_OK;
+    case VX_OP_FULL_DECODE:
+      *bytes = plan_decode(kv, batch, max_pages_eff(kv, batch), false).ws_bytes();
+      return VX_OK;
+  }
+  return VX_ERR_INVALID_ARGUMENT;
+}
+
+vx_status vx_set_pages_per_split(int32_t pages_per_split) {
+  if (pages_per_split < 0) return VX_ERR_INVALID_ARGUMENT;
+  g_pages_per_split_override = pages_per_split;
+  return VX_OK;
+}
+
+const char* vx_status_string(vx_status status) {
+  switch (status) {
+    case VX_OK: return "ok";
+    case VX_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case VX_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case VX_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case VX_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t vx_version(void) { return 100; }
+
+}  // extern "C"

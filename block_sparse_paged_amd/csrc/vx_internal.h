@@ -1,0 +1,73 @@
+// Internal interface between the C-ABI layer (vx_api.cpp) and the kernel
+// translation units.  Launchers return hipErrorInvalidValue when no kernel
+// instance matches the shape; the API layer validates shapes first.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vx {
+
+// Kernel argument blocks are passed by value.
+
+struct CentroidArgs {
+  const void* k;          // [P, H_kv, S_p, D]
+  void* cent;             // [P, H_kv, D]
+  const int32_t* ids;     // [n_ids]
+  int32_t n_ids, H_kv, S_p, D;
+};
+
+struct ScoreArgs {
+  const void* q;          // [B, H_q, D]
+  const void* cent;       // [P, H_kv, D]
+  const int32_t* pt;      // [B, pt_stride]
+  const int32_t* seq_lens;
+  float* scores;          // [B, H_kv, score_stride], candidate-indexed
+  int32_t B, H_q, H_kv, D, S_p, pt_stride, score_stride, max_tokens;
+  int32_t n_bos, n_eos;
+  int32_t cand_per_block;
+};
+
+struct TopkArgs {
+  const float* scores;    // [B, H_kv, score_stride]
+  const int32_t* seq_lens;
+  int32_t* sel;           // [B, H_kv, k_tot]
+  int32_t B, H_kv, S_p, score_stride, max_tokens;
+  int32_t topk, n_bos, n_eos, k_tot;
+};
+
+struct DecodeArgs {
+  const void* q;          // [B, H_q, D_qk]
+  const void* k;          // [P, H_kv, S_p, D_qk]
+  const void* v;          // [P, H_kv, S_p, D_v] (may alias k)
+  const int32_t* pt;      // [B, pt_stride]
+  const int32_t* seq_lens;
+  const int32_t* sel;     // [B, H_kv, k_tot] or nullptr for every page
+  float* part_o;          // [B, H_q, n_split, D_v] fp32 (split mode)
+  float* part_ml;         // [B, H_q, n_split, 2]  (max in log2 units, sum)
+  void* out;              // [B, H_q, D_v] (direct mode)
+  float* lse;             // [B, H_q] or nullptr (direct mode)
+  int32_t B, H_q, H_kv, S_p, pt_stride, k_tot, max_tokens;
+  int32_t pages_per_split, n_split;
+  int32_t v_stride_tok;   // elements between consecutive tokens of V (D_qk when aliased)
+  float scale_log2;       // sm_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  void* out;
+  float* lse;
+  int32_t B, H_q, n_split, D_v;
+};
+
+hipError_t launch_centroid(int dtype, const CentroidArgs& a, hipStream_t s);
+hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s);
+// D = D_qk = D_v for this path; G = H_q / H_kv.
+hipError_t launch_decode_valu(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
+
+}  // namespace vx

@@ -1,0 +1,210 @@
+/*
+ * vx.h - C ABI of libvx: centroid-indexed block-top-k sparse decode attention
+ * over a paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Vortex, "Efficient and Programmable Sparse Attention Serving
+ * for AI Agents"; article section "A dual-stage programmable abstraction",
+ * and the vortex_torch README section "Quick Example: Custom Sparse
+ * Attention") runs in two stages:
+ *   - query-independent: when a KV page fills up, the mean of its keys (its
+ *     centroid) is stored in a per-page centroid table      -> vx_centroid_update
+ *   - query-dependent, every decode step: the query is averaged over the
+ *     query heads of each KV head, dotted with the centroids of the
+ *     request's pages, and the top-k pages (plus reserved first and last
+ *     pages) are chosen                                      -> vx_score_topk
+ *     then exact attention runs over only those pages        -> vx_sparse_paged_decode
+ * Full attention over every page is the baseline the method is measured
+ * against, and what a skipped layer runs (README, "Using Your Sparse
+ * Attention with SGLang")                                    -> vx_full_paged_decode
+ *
+ * Conventions shared by every call
+ *   Pointers.   Every buffer pointer is a DEVICE pointer unless marked
+ *               "host".  Structs are read on the host during the call
+ *               only and are not retained.
+ *   Ownership.  The caller owns every buffer.  The library never
+ *               allocates or frees device memory and keeps no state across
+ *               calls except cached device properties and the split
+ *               override below; calls are reentrant.
+ *   Streams.    Work is enqueued on `stream` (NULL = the null stream);
+ *               calls return after launch, never synchronise the host.
+ *   Errors.     Arguments are validated on the host before any HIP call;
+ *               on error nothing is launched and a vx_status is returned.
+ *               A failed launch returns VX_ERR_HIP.  Device-side contract
+ *               violations (page ids >= num_pages, seq_lens above
+ *               max_seq_len or below 1, a page table that does not cover a
+ *               sequence) are undefined behaviour.
+ *   Determinism. Identical inputs give bit-identical outputs (fixed plan
+ *               per shape, no floating-point atomics).
+ *
+ * Data layout in HBM (all row-major, contiguous):
+ *   K pool       [P, H_kv, S_p, D_qk]   dtype     (head-major pages)
+ *   V pool       [P, H_kv, S_p, D_v]    dtype     (or aliased into K, MLA)
+ *   centroids    [P, H_kv, D_qk]        dtype     one row per page and KV head
+ *   page_table   [B, max_pages] int32   physical page of logical page p
+ *   seq_lens     [B] int32              tokens incl. the one being decoded
+ *   q            [B, H_q, D_qk]         dtype     query head j uses KV head j / G
+ *   sel          [B, H_kv, k_tot] int32 logical pages, ascending, -1 padded
+ *   out          [B, H_q, D_v]          dtype
+ *   lse          [B, H_q] float32       natural log of the softmax denominator
+ *
+ * Supported shapes (others return VX_ERR_UNSUPPORTED):
+ *   dtype VX_F32 or VX_BF16, page_size 16 or 64, H_q = G * H_kv with
+ *   G in {1, 2, 4, 8} for D_qk = D_v in {64, 128};
+ *   MLA: VX_BF16, D_qk = 576, D_v = 512, v_aliases_k = 1, H_kv = 1,
+ *   page_size 64, H_q <= 32.
+ */
+#ifndef VX_H
+#define VX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VX_OK = 0,
+  VX_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, negative size, inconsistent shape */
+  VX_ERR_UNSUPPORTED = 2,        /* valid but not a shape/dtype this build handles  */
+  VX_ERR_WORKSPACE_TOO_SMALL = 3,
+  VX_ERR_HIP = 4                 /* a HIP runtime call or launch failed             */
+} vx_status;
+
+typedef enum { VX_F32 = 0, VX_BF16 = 1 } vx_dtype;
+
+/* Operation ids for vx_workspace_size. */
+typedef enum {
+  VX_OP_SCORE_TOPK = 0,
+  VX_OP_SPARSE_DECODE = 1,
+  VX_OP_FULL_DECODE = 2
+} vx_op;
+
+/* The paged KV cache and its named centroid cache (the per-page summary
+ * table the cache stage writes; README "Quick Example": one head_dim-wide
+ * row per page). */
+typedef struct {
+  int32_t dtype;          /* vx_dtype of K, V, centroids, q and out           */
+  int32_t num_pages;      /* P, physical pages in the pool                     */
+  int32_t page_size;      /* S_p, tokens per page: 16 or 64                    */
+  int32_t num_kv_heads;   /* H_kv                                              */
+  int32_t head_dim_qk;    /* D_qk                                              */
+  int32_t head_dim_v;     /* D_v                                               */
+  int32_t v_aliases_k;    /* 1: V is K[..., :D_v] and v_cache must be NULL     */
+  int32_t reserved_;      /* must be 0                                         */
+  const void* k_cache;    /* [P, H_kv, S_p, D_qk]                              */
+  const void* v_cache;    /* [P, H_kv, S_p, D_v], or NULL when v_aliases_k     */
+  void* centroids;        /* [P, H_kv, D_qk]                                   */
+} vx_paged_kv;
+
+/* One decode batch: the page-table metadata of the article's section "The
+ * friction of paged memory" (a logical sequence spread over physical pages). */
+typedef struct {
+  int32_t batch;              /* B; 0 is allowed: nothing is read or launched
+                                 and the device pointers may be NULL            */
+  int32_t num_q_heads;        /* H_q, a multiple of H_kv                         */
+  int32_t max_pages_per_req;  /* row stride of page_table                        */
+  int32_t max_seq_len;        /* host-side bound on every seq_lens[b], used to
+                                 plan the launch; max_pages_per_req * page_size
+                                 must be >= max_seq_len                         */
+  const int32_t* page_table;  /* [B, max_pages_per_req]                          */
+  const int32_t* seq_lens;    /* [B], each in [1, max_seq_len]                   */
+} vx_batch;
+
+/* Query-independent stage (article, "A dual-stage programmable
+ * abstraction": centroids computed while the cache is built, stored and
+ * reused across steps; README "Quick Example": CMean over the keys of a
+ * page, run only when a page is finished).
+ *
+ * For each listed physical page p and KV head h:
+ *   centroids[p, h, :] = round_to_dtype( (1/S_p) * sum_t K[p, h, t, :] )
+ * summed in fp32 and rounded once (round to nearest even).
+ *   page_ids  device int32 [n_ids], each in [0, num_pages); every listed page
+ *             must hold S_p valid tokens.  Duplicates are allowed.
+ *   n_ids     >= 0; 0 launches nothing.
+ * Only kv->k_cache and kv->centroids are touched. */
+vx_status vx_centroid_update(const vx_paged_kv* kv, const int32_t* page_ids,
+                             int32_t n_ids, hipStream_t stream);
+
+/* Query-dependent indexer (README "Quick Example": mean of the query over
+ * heads, GeMV against the centroids, topK into the page index structure;
+ * README "Using Your Sparse Attention with SGLang": top-k value and the
+ * reserved BOS / EOS page counts).
+ *
+ * For request b with n_b = ceil(seq_lens[b] / S_p) logical pages and KV
+ * head h:
+ *   qbar      = mean of q[b, h*G : (h+1)*G, :]           (fp32)
+ *   reserved  = pages [0, n_bos) and [n_b - n_eos, n_b)
+ *   candidates= pages [n_bos, n_b - n_eos)   (all full pages, need centroids)
+ *   score[p]  = dot(qbar, centroids[page_table[b, p], h, :])  (fp32)
+ *   top       = the topk candidates of largest score, equal scores going
+ *               to the lower logical page (all candidates if fewer)
+ *   sel[b, h, :] = reserved U top, ascending, then -1 up to k_tot
+ * with k_tot = topk + n_bos + n_eos.
+ *   q          device [B, H_q, D_qk], dtype
+ *   topk >= 0, n_bos >= 0, n_eos >= 1 (the last page may be partial and has
+ *              no centroid, so it must be reserved)
+ *   sel        device int32 [B, H_kv, k_tot], written completely
+ *   workspace  device scratch of at least
+ *              vx_workspace_size(VX_OP_SCORE_TOPK, ...) bytes; contents on
+ *              entry do not matter.
+ * Candidates per request are limited to 16384 pages (VX_ERR_UNSUPPORTED). */
+vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                        int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Sparse attention over the selected pages (article, "A dual-stage
+ * programmable abstraction": after selecting the top-k blocks the system
+ * performs the actual attention on them).
+ *
+ * For query head j of request b (KV head h = j / G), over the tokens
+ * {(p, t) : p in sel[b, h, :], p >= 0, t < S_p, p*S_p + t < seq_lens[b]}:
+ *   l_t = sm_scale * dot(q[b, j], K[page_table[b, p], h, t])
+ *   out[b, j] = sum_t softmax(l)_t * V[page_table[b, p], h, t]
+ *   lse[b, j] = log(sum_t exp(l_t))
+ * Split-K flash decoding: each (request, KV head) is cut into splits of
+ * whole pages whose fp32 partials (o, max, sum) are merged exactly.
+ *   sel        device int32 [B, H_kv, k_tot] as written by vx_score_topk:
+ *              valid entries are a prefix; the first negative entry ends it
+ *   out        device [B, H_q, D_v], dtype
+ *   lse        device float32 [B, H_q], or NULL
+ *   workspace  at least vx_workspace_size(VX_OP_SPARSE_DECODE, ...) bytes
+ * A request with no selected page gets out = 0 and lse = -inf. */
+vx_status vx_sparse_paged_decode(const vx_paged_kv* kv, const vx_batch* batch,
+                                 const void* q, const int32_t* sel, int32_t k_tot,
+                                 float sm_scale, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Full paged attention over every page of every request: the baseline
+ * (README, "Using Your Sparse Attention with SGLang": with sparsity off, or
+ * for a skipped layer, full attention is used).  Same definition as
+ * vx_sparse_paged_decode with sel = all n_b pages.
+ *   workspace  at least vx_workspace_size(VX_OP_FULL_DECODE, ...) bytes */
+vx_status vx_full_paged_decode(const vx_paged_kv* kv, const vx_batch* batch,
+                               const void* q, float sm_scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Workspace bytes the call `op` needs for these shapes (k_tot is read for
+ * VX_OP_SPARSE_DECODE only).  Host-only; never touches the GPU.  The size
+ * depends on the shapes and on the split override, nothing else. */
+vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* batch,
+                            int32_t k_tot, size_t* bytes /* host */);
+
+/* Test hook: force every decode split to cover `pages_per_split` pages
+ * (0 restores the planner).  Process-wide; not for concurrent use with
+ * other calls.  Returns VX_ERR_INVALID_ARGUMENT for a negative value. */
+vx_status vx_set_pages_per_split(int32_t pages_per_split);
+
+/* Static, NUL-terminated description of a status code. */
+const char* vx_status_string(vx_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t vx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VX_H */

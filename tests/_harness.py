@@ -1,0 +1,249 @@
+"""Test plumbing shared by the GPU parity tests: sets up a workload on the
+device through the library's binding, draws queries whose k-th / (k+1)-th
+page-score gap is large enough for the selected set to be unique, and runs
+the fp64 oracle request by request on the same bytes.
+
+The gap rule: for every (request, KV head) whose candidate count exceeds k,
+the fp64 oracle scores must satisfy  s_(k) - s_(k+1) > 1e-3 * max|s|  over
+the candidates.  Groups that fail are redrawn (attempt 1, 2, ...) from the
+seeded generator.  The margin dwarfs the fp32 scoring error and a one-ulp
+bf16 centroid disagreement, so any set mismatch is a bug.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle as orc
+import synth
+
+GAP_REL = 1e-3
+MAX_ATTEMPTS = 1000
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (normal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - 7)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+@dataclass
+class Case:
+    w: synth.Workload
+    layout: synth.PageLayout
+    K: torch.Tensor
+    V: torch.Tensor | None
+    cent: torch.Tensor
+    pt: torch.Tensor
+    seq_lens: torch.Tensor
+    kv: object
+    step: int = 0
+    q_host: torch.Tensor | None = None          # [B, H_q, D] in the workload dtype
+    attempts: np.ndarray | None = None
+    _oracle_cent: dict = field(default_factory=dict)
+
+    @property
+    def L(self) -> np.ndarray:
+        return synth.step_seq_lens(self.layout, self.step)
+
+    def batch(self, vx):
+        return vx.Batch(page_table=self.pt, seq_lens=self.seq_lens,
+                        num_q_heads=self.w.num_q_heads,
+                        max_seq_len=int(self.layout.seq_lens0.max()) + self.w.steps - 1)
+
+    def n_pages(self, b: int) -> int:
+        return -(-int(self.L[b]) // self.w.page_size)
+
+    def request_pages(self, b: int):
+        """Logical view of request b's pages on the host (fp64): K, V."""
+        n = -(-int(self.layout.seq_lens0[b] + self.w.steps - 1) // self.w.page_size)
+        idx = self.pt[b, :n].long()
+        k = to_f64(self.K[idx])
+        v = None if self.V is None else to_f64(self.V[idx])
+        return k, v
+
+    def oracle_centroids(self, b: int, k_pages=None) -> np.ndarray:
+        """Oracle centroids of request b's logical pages at the current step."""
+        key = (b, int(self.L[b]) // self.w.page_size)
+        if key not in self._oracle_cent:
+            if k_pages is None:
+                k_pages, _ = self.request_pages(b)
+            self._oracle_cent[key] = orc.request_centroids(k_pages, int(self.L[b]), self.w.dtype)
+        return self._oracle_cent[key]
+
+
+def setup_case(vx, w: synth.Workload, device="cuda") -> Case:
+    lay = synth.build_layout(w)
+    K, V = synth.make_kv_pool(w, lay, device=device)
+    cent = torch.zeros((lay.num_pages, w.num_kv_heads, w.head_dim_qk), dtype=w.torch_dtype,
+                       device=device)
+    pt = torch.from_numpy(lay.page_table).to(device)
+    sl = torch.from_numpy(synth.step_seq_lens(lay, 0).astype(np.int32)).to(device)
+    kv = vx.PagedKV(k_cache=K, v_cache=V, centroids=cent, head_dim_v=w.head_dim_v)
+    c = Case(w=w, layout=lay, K=K, V=V, cent=cent, pt=pt, seq_lens=sl, kv=kv)
+    c.attempts = np.zeros((w.batch, w.num_kv_heads), dtype=np.int64)
+    c.q_host = synth.make_queries(w, lay, 0)
+    return c
+
+
+def set_step(c: Case, step: int):
+    c.step = step
+    c.seq_lens.copy_(torch.from_numpy(synth.step_seq_lens(c.layout, step).astype(np.int32)))
+    c.attempts[:] = 0
+    c.q_host = synth.make_queries(c.w, c.layout, step)
+
+
+def gap_ok(scores: np.ndarray, k: int) -> bool:
+    if len(scores) <= k or k == 0:
+        return True
+    s = np.sort(scores)[::-1]
+    return (s[k - 1] - s[k]) > GAP_REL * np.max(np.abs(scores))
+
+
+def fix_gaps(c: Case, requests) -> int:
+    """Redraw query groups of the listed requests until every group's score
+    gap is wide enough.  Returns the number of redraws."""
+    w = c.w
+    G = w.group
+    redraws = 0
+    for b in requests:
+        n_b = c.n_pages(b)
+        cand = orc.candidate_pages(n_b, w.n_bos, w.n_eos)
+        if len(cand) <= w.topk:
+            continue
+        cent = c.oracle_centroids(b)
+        for h in range(w.num_kv_heads):
+            while True:
+                q = c.q_host[b, h * G:(h + 1) * G].to(torch.float64).numpy()
+                qbar = orc.group_mean_query(q, 1)
+                s = orc.page_scores(qbar, cent[:, h:h + 1], cand)[0]
+                if gap_ok(s, w.topk):
+                    break
+                c.attempts[b, h] += 1
+                redraws += 1
+                if c.attempts[b, h] > MAX_ATTEMPTS:
+                    raise RuntimeError(f"no query draw with a score gap for ({b},{h})")
+                g = synth.draw_query_group(w, c.layout, c.step, b, h, int(c.attempts[b, h]))
+                c.q_host[b, h * G:(h + 1) * G] = torch.from_numpy(g).to(w.torch_dtype)
+    return redraws
+
+
+def oracle_request(c: Case, b: int, sparse: bool = True):
+    """(selection table [H_kv, k_tot] or None, o [H_q, D_v], lse [H_q])."""
+    w = c.w
+    k, v = c.request_pages(b)
+    q = c.q_host[b].to(torch.float64).numpy()
+    L = int(c.L[b])
+    vd = w.head_dim_v if v is None else None
+    if sparse:
+        cent = c.oracle_centroids(b, k)
+        sel, o, lse = orc.sparse_decode_request(q, k, v, cent, L, w.sm_scale, w.topk,
+                                                w.n_bos, w.n_eos, v_dims=vd)
+        return orc.selection_table(sel, w.k_tot), o, lse
+    o, lse = orc.decode_request(q, k, v, L, w.sm_scale, None, v_dims=vd)
+    return None, o, lse
+
+
+def out_tolerance(dtype: str):
+    """(max-abs, relative L2) bounds for outputs; lse bound."""
+    if dtype == "f32":
+        return 1e-4, 1e-5, 1e-4
+    return 2e-2, 1e-2, 1e-3
+
+
+def assert_close_out(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
+    ma, rel, _ = out_tolerance(dtype)
+    d = np.abs(got - want)
+    err = float(d.max()) if d.size else 0.0
+    r = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
+    assert err <= ma and r <= rel, f"{what}: max|d|={err:.3g} (<= {ma}), rel={r:.3g} (<= {rel})"
+
+
+def assert_close_lse(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
+    tol = out_tolerance(dtype)[2]
+    d = float(np.max(np.abs(got - want)))
+    assert d <= tol, f"{what}: lse max|d|={d:.3g} (<= {tol})"
+
+
+def assert_centroids(c: Case, pages_phys: np.ndarray):
+    """GPU centroid rows of the listed physical pages vs the oracle."""
+    if len(pages_phys) == 0:
+        return
+    idx = torch.from_numpy(pages_phys.astype(np.int64)).to(c.K.device)
+    got = to_f64(c.cent[idx])
+    kp = to_f64(c.K[idx])
+    want = orc.page_centroids(kp, c.w.dtype)
+    if c.w.dtype == "bf16":
+        tol = np.maximum(bf16_ulp(want), 2.0 ** -20)
+    else:
+        tol = 2e-6 * np.abs(kp).mean(axis=2) + 2.0 ** -24 * np.abs(want)
+    bad = np.abs(got - want) > tol
+    assert not bad.any(), f"{int(bad.sum())} centroid elements off by more than the bound"
+
+
+def run_indexer(vx, c: Case, q_dev: torch.Tensor, ws=None):
+    w = c.w
+    bt = c.batch(vx)
+    sel = torch.empty((w.batch, w.num_kv_heads, w.k_tot), dtype=torch.int32, device=q_dev.device)
+    if ws is None:
+        ws = vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, c.kv, bt)
+    vx.score_topk(c.kv, bt, q_dev, w.topk, w.n_bos, w.n_eos, sel, ws)
+    return sel
+
+
+def run_sparse(vx, c: Case, q_dev, sel, ws=None):
+    w = c.w
+    bt = c.batch(vx)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype,
+                      device=q_dev.device)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=q_dev.device)
+    if ws is None:
+        ws = vx.alloc_workspace(vx.VX_OP_SPARSE_DECODE, c.kv, bt, w.k_tot)
+    vx.sparse_paged_decode(c.kv, bt, q_dev, sel, w.sm_scale, out, lse, ws)
+    return out, lse
+
+
+def run_full(vx, c: Case, q_dev, ws=None):
+    w = c.w
+    bt = c.batch(vx)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype,
+                      device=q_dev.device)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=q_dev.device)
+    if ws is None:
+        ws = vx.alloc_workspace(vx.VX_OP_FULL_DECODE, c.kv, bt)
+    vx.full_paged_decode(c.kv, bt, q_dev, w.sm_scale, out, lse, ws)
+    return out, lse
+
+
+def build_centroids(vx, c: Case):
+    """Bulk centroids of every page full before step 0, then step 0's completions."""
+    ids = np.concatenate([synth.setup_full_pages(c.layout), synth.completed_pages(c.layout, 0)])
+    t = torch.from_numpy(ids.astype(np.int32)).to(c.K.device)
+    vx.centroid_update(c.kv, t)
+    return ids
+
+
+def sample_requests(B: int, n: int = 3):
+    if B <= n:
+        return list(range(B))
+    return sorted({0, B - 1, *range(B // n, B - 1, max(1, B // n))})[:n + 1]
+
+
+def describe(w) -> str:
+    return (f"{w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+            f"D={w.head_dim_qk}/{w.head_dim_v} Sp={w.page_size} {w.dtype} k={w.topk}")
+
+
+def log(msg: str):
+    print(msg, flush=True)
+
+
+__all__ = [n for n in dir() if not n.startswith("_")] + ["math"]

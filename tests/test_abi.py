@@ -1,0 +1,216 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, and rejects invalid arguments before any HIP call (nothing
+here launches a kernel, so it runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_paged_amd as vx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000                      # never dereferenced: validation fails first
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "vx.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vx_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vx.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(vx.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert vx.status_string(0) == "ok"
+    assert "workspace" in vx.status_string(3)
+    assert vx.status_string(99) == "unknown status"
+    assert vx.version() >= 100
+
+
+def kv_struct(**kw):
+    d = dict(dtype=vx.VX_BF16, num_pages=64, page_size=16, num_kv_heads=8, head_dim_qk=128,
+             head_dim_v=128, v_aliases_k=0, reserved_=0, k_cache=FAKE, v_cache=FAKE,
+             centroids=FAKE)
+    d.update(kw)
+    return vx.PagedKVStruct(**d)
+
+
+def batch_struct(**kw):
+    d = dict(batch=4, num_q_heads=16, max_pages_per_req=64, max_seq_len=1024,
+             page_table=FAKE, seq_lens=FAKE)
+    d.update(kw)
+    return vx.BatchStruct(**d)
+
+
+def ws_size(lib, op, kv, bt, k_tot=32):
+    out = ctypes.c_size_t(0)
+    st = lib.vx_workspace_size(op, ctypes.byref(kv), ctypes.byref(bt), k_tot, ctypes.byref(out))
+    return st, out.value
+
+
+BAD_KV = [
+    (dict(dtype=7), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=0), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(num_kv_heads=0), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(reserved_=1), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(page_size=32), vx.VX_ERR_UNSUPPORTED),
+    (dict(head_dim_qk=96, head_dim_v=96), vx.VX_ERR_UNSUPPORTED),
+    (dict(head_dim_v=64), vx.VX_ERR_UNSUPPORTED),
+    (dict(v_aliases_k=1), vx.VX_ERR_INVALID_ARGUMENT),            # v_cache must be NULL
+    (dict(v_aliases_k=2), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(head_dim_qk=576, head_dim_v=512, v_aliases_k=1, v_cache=None, num_kv_heads=1,
+          page_size=64, dtype=vx.VX_F32), vx.VX_ERR_UNSUPPORTED),
+]
+
+BAD_BATCH = [
+    (dict(batch=-1), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(num_q_heads=12), vx.VX_ERR_INVALID_ARGUMENT),           # not a multiple of H_kv
+    (dict(num_q_heads=24), vx.VX_ERR_UNSUPPORTED),                # G = 3
+    (dict(max_seq_len=0), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(max_pages_per_req=0), vx.VX_ERR_INVALID_ARGUMENT),
+    (dict(max_seq_len=1025), vx.VX_ERR_INVALID_ARGUMENT),         # 64 pages * 16 < 1025
+]
+
+
+@pytest.mark.parametrize("kw,want", BAD_KV)
+def test_bad_kv_rejected_everywhere(lib, kw, want):
+    kv, bt = kv_struct(**kw), batch_struct()
+    r = ctypes.byref
+    assert lib.vx_centroid_update(r(kv), FAKE, 4, None) == want
+    assert lib.vx_score_topk(r(kv), r(bt), FAKE, 30, 1, 1, FAKE, FAKE, 1 << 30, None) == want
+    assert lib.vx_sparse_paged_decode(r(kv), r(bt), FAKE, FAKE, 32, 0.1, FAKE, FAKE, FAKE,
+                                      1 << 30, None) == want
+    assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == want
+    assert ws_size(lib, vx.VX_OP_FULL_DECODE, kv, bt)[0] == want
+
+
+@pytest.mark.parametrize("kw,want", BAD_BATCH)
+def test_bad_batch_rejected(lib, kw, want):
+    kv, bt = kv_struct(), batch_struct(**kw)
+    r = ctypes.byref
+    assert lib.vx_score_topk(r(kv), r(bt), FAKE, 30, 1, 1, FAKE, FAKE, 1 << 30, None) == want
+    assert lib.vx_sparse_paged_decode(r(kv), r(bt), FAKE, FAKE, 32, 0.1, FAKE, FAKE, FAKE,
+                                      1 << 30, None) == want
+    assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == want
+    for op in (0, 1, 2):
+        assert ws_size(lib, op, kv, bt)[0] == want
+
+
+def test_null_pointers_rejected(lib):
+    r = ctypes.byref
+    kv, bt = kv_struct(), batch_struct()
+    assert lib.vx_centroid_update(None, FAKE, 1, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert lib.vx_centroid_update(r(kv), None, 1, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert lib.vx_centroid_update(r(kv_struct(centroids=None)), FAKE, 1, None) == 1
+    assert lib.vx_score_topk(r(kv), None, FAKE, 30, 1, 1, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.vx_score_topk(r(kv), r(bt), None, 30, 1, 1, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.vx_score_topk(r(kv), r(bt), FAKE, 30, 1, 1, None, FAKE, 1 << 30, None) == 1
+    assert lib.vx_score_topk(r(kv), r(bt), FAKE, 30, 1, 1, FAKE, None, 1 << 30, None) == 1
+    assert lib.vx_score_topk(r(kv), r(batch_struct(page_table=None)), FAKE, 30, 1, 1, FAKE,
+                             FAKE, 1 << 30, None) == 1
+    assert lib.vx_sparse_paged_decode(r(kv), r(bt), FAKE, None, 32, 0.1, FAKE, FAKE, FAKE,
+                                      1 << 30, None) == 1
+    assert lib.vx_sparse_paged_decode(r(kv), r(bt), FAKE, FAKE, 32, 0.1, None, FAKE, FAKE,
+                                      1 << 30, None) == 1
+    assert lib.vx_full_paged_decode(r(kv_struct(v_cache=None)), r(bt), FAKE, 0.1, FAKE,
+                                    FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.vx_workspace_size(0, r(kv), r(bt), 32, None) == 1
+
+
+def test_scalar_arguments_rejected(lib):
+    r = ctypes.byref
+    kv, bt = kv_struct(), batch_struct()
+    for topk, bos, eos in ((-1, 1, 1), (30, -1, 1), (30, 1, 0)):
+        assert lib.vx_score_topk(r(kv), r(bt), FAKE, topk, bos, eos, FAKE, FAKE, 1 << 30,
+                                 None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert lib.vx_centroid_update(r(kv), FAKE, -1, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert lib.vx_centroid_update(r(kv), None, 0, None) == vx.VX_OK      # nothing to do
+    for k_tot in (0, -3):
+        assert lib.vx_sparse_paged_decode(r(kv), r(bt), FAKE, FAKE, k_tot, 0.1, FAKE, FAKE,
+                                          FAKE, 1 << 30, None) == 1
+    for scale in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, scale, FAKE, FAKE, FAKE, 1 << 30,
+                                        None) == 1
+    assert lib.vx_set_pages_per_split(-1) == vx.VX_ERR_INVALID_ARGUMENT
+    assert lib.vx_workspace_size(9, r(kv), r(bt), 32, r(ctypes.c_size_t())) == 1
+
+
+def test_workspace_too_small_rejected(lib):
+    r = ctypes.byref
+    kv = kv_struct()
+    bt = batch_struct(batch=64, max_pages_per_req=2048, max_seq_len=32768)
+    st, need = ws_size(lib, vx.VX_OP_SCORE_TOPK, kv, bt)
+    assert st == 0 and need >= 64 * 8 * 2048 * 4
+    assert lib.vx_score_topk(r(kv), r(bt), FAKE, 30, 1, 1, FAKE, FAKE, need - 1, None) == 3
+    st, need = ws_size(lib, vx.VX_OP_FULL_DECODE, kv, bt)
+    assert st == 0 and need > 0
+    assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, 0.1, FAKE, FAKE, FAKE, need - 1,
+                                    None) == 3
+    st, need = ws_size(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32)
+    assert st == 0
+    if need:
+        assert lib.vx_sparse_paged_decode(r(kv), r(bt), FAKE, FAKE, 32, 0.1, FAKE, FAKE, FAKE,
+                                          need - 1, None) == 3
+
+
+def test_empty_batch_launches_nothing(lib):
+    r = ctypes.byref
+    kv, bt = kv_struct(), batch_struct(batch=0)
+    assert lib.vx_score_topk(r(kv), r(bt), FAKE, 30, 1, 1, FAKE, FAKE, 1 << 30, None) == 0
+    assert lib.vx_sparse_paged_decode(r(kv), r(bt), FAKE, FAKE, 32, 0.1, FAKE, FAKE, FAKE,
+                                      1 << 30, None) == 0
+    assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == 0
+
+
+def test_too_many_candidates_unsupported(lib):
+    kv = kv_struct()
+    bt = batch_struct(max_pages_per_req=20000, max_seq_len=20000 * 16)
+    assert ws_size(lib, vx.VX_OP_SCORE_TOPK, kv, bt)[0] == vx.VX_ERR_UNSUPPORTED
+
+
+def test_workspace_monotone_in_shapes(lib):
+    kv = kv_struct()
+    prev = 0
+    for B in (1, 4, 16, 64, 256):
+        bt = batch_struct(batch=B, max_pages_per_req=4096, max_seq_len=65536)
+        st, n = ws_size(lib, vx.VX_OP_SCORE_TOPK, kv, bt)
+        assert st == 0 and n >= prev
+        prev = n
+    for op, kt in ((vx.VX_OP_SPARSE_DECODE, 66), (vx.VX_OP_FULL_DECODE, 0)):
+        sizes = []
+        for L in (1024, 8192, 65536):
+            bt = batch_struct(batch=32, max_pages_per_req=4096, max_seq_len=L)
+            st, n = ws_size(lib, op, kv, bt, kt)
+            assert st == 0
+            sizes.append(n)
+        assert sizes == sorted(sizes) or op == vx.VX_OP_SPARSE_DECODE
+
+
+def test_split_override_changes_plan(lib):
+    kv = kv_struct()
+    bt = batch_struct(batch=2, max_pages_per_req=256, max_seq_len=4096)
+    try:
+        assert lib.vx_set_pages_per_split(1) == 0
+        _, n1 = ws_size(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32)
+        assert n1 >= 2 * 16 * 32 * 128 * 4                  # 32 splits of fp32 partials
+        assert lib.vx_set_pages_per_split(1000) == 0
+        _, n2 = ws_size(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32)
+        assert n2 == 0                                      # one split: direct output
+    finally:
+        lib.vx_set_pages_per_split(0)

@@ -1,0 +1,288 @@
+"""GPU parity: every libvx call against the fp64 oracle on the same seeded
+bytes.  Page selections must be bit-exact; outputs must be within 2e-2
+max-abs and 1e-2 relative L2 (bf16 inputs, fp32 accumulation; fp32 inputs:
+1e-4 / 1e-5), lse within 1e-3 (fp32: 1e-4); centroids within one bf16 unit
+in the last place of the oracle's rounded mean.
+
+Small workloads run whole; full-size workloads run in the launch
+configuration the benchmark uses, checked on sampled requests."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle as orc
+from tests import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_paged_amd as m
+    m.load_library()
+    m.set_pages_per_split(0)
+    return m
+
+
+SMALL = list(synth.SMALL_WORKLOADS)
+
+
+def _mla_guard(vx, w):
+    if w.structure == "mla" and not mla_supported(vx):
+        pytest.skip("MLA decode kernel not in this build")
+
+
+def mla_supported(vx):
+    import ctypes
+    kv = vx.PagedKVStruct(dtype=1, num_pages=1, page_size=64, num_kv_heads=1, head_dim_qk=576,
+                          head_dim_v=512, v_aliases_k=1, reserved_=0, k_cache=1, v_cache=None,
+                          centroids=1)
+    bt = vx.BatchStruct(batch=1, num_q_heads=32, max_pages_per_req=1, max_seq_len=64,
+                        page_table=1, seq_lens=1)
+    n = ctypes.c_size_t()
+    return vx.load_library().vx_workspace_size(2, ctypes.byref(kv), ctypes.byref(bt), 0,
+                                               ctypes.byref(n)) == 0
+
+
+def _prepared(vx, name, requests=None):
+    w = synth.get_workload(name)
+    _mla_guard(vx, w)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_centroids(vx, c)
+    reqs = range(w.batch) if requests is None else requests
+    H.fix_gaps(c, reqs)
+    return c, reqs
+
+
+def _check_request(vx, c, b, sel_dev, out, lse, sparse=True):
+    sel_ref, o_ref, lse_ref = H.oracle_request(c, b, sparse)
+    if sparse:
+        got = sel_dev[b].cpu().numpy()
+        assert np.array_equal(got, sel_ref), f"request {b}: selected pages differ"
+    H.assert_close_out(H.to_f64(out[b]), o_ref, c.w.dtype, f"request {b} out")
+    H.assert_close_lse(H.to_f64(lse[b]), lse_ref, c.w.dtype, f"request {b}")
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_centroids_small(vx, name):
+    w = synth.get_workload(name)
+    _mla_guard(vx, w)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    ids = H.build_centroids(vx, c)
+    torch.cuda.synchronize()
+    H.assert_centroids(c, ids)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_sparse_step_small(vx, name):
+    c, reqs = _prepared(vx, name)
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    out, lse = H.run_sparse(vx, c, q, sel)
+    torch.cuda.synchronize()
+    for b in reqs:
+        _check_request(vx, c, b, sel, out, lse)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_full_decode_small(vx, name):
+    c, reqs = _prepared(vx, name)
+    q = c.q_host.cuda()
+    out, lse = H.run_full(vx, c, q)
+    torch.cuda.synchronize()
+    for b in reqs:
+        _check_request(vx, c, b, None, out, lse, sparse=False)
+
+
+@pytest.mark.parametrize("name", ["qwen3_small", "long_small", "mla_small"])
+def test_repeat_runs_bit_identical(vx, name):
+    c, _ = _prepared(vx, name)
+    q = c.q_host.cuda()
+    a = [H.run_indexer(vx, c, q)]
+    a += list(H.run_sparse(vx, c, q, a[0]))
+    a += list(H.run_full(vx, c, q))
+    b = [H.run_indexer(vx, c, q)]
+    b += list(H.run_sparse(vx, c, q, b[0]))
+    b += list(H.run_full(vx, c, q))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["tiny_b1_l1k_f32", "qwen3_small", "long_small", "mla_small"])
+def test_split_count_does_not_change_result(vx, name):
+    c, _ = _prepared(vx, name)
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    base = H.run_sparse(vx, c, q, sel) + H.run_full(vx, c, q)
+    tol = 1e-5 if c.w.dtype == "f32" else 1e-2
+    try:
+        for pps in (1, 3, 100000):
+            vx.set_pages_per_split(pps)
+            alt = H.run_sparse(vx, c, q, sel) + H.run_full(vx, c, q)
+            torch.cuda.synchronize()
+            for x, y in zip(base, alt):
+                d = (x.float() - y.float()).abs().max().item()
+                assert d <= tol, f"pages_per_split={pps}: max|d|={d}"
+    finally:
+        vx.set_pages_per_split(0)
+
+
+@pytest.mark.parametrize("name", ["tiny_b1_l1k_f32", "qwen3_small", "mla_small"])
+def test_sparse_equals_full_when_topk_covers_all(vx, name):
+    w = synth.get_workload(name)
+    _mla_guard(vx, w)
+    w = w.with_(topk=100000)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_centroids(vx, c)
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    so, sl = H.run_sparse(vx, c, q, sel)
+    fo, fl = H.run_full(vx, c, q)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        n = c.n_pages(b)
+        assert sel[b, :, :n].cpu().tolist() == [list(range(n))] * w.num_kv_heads
+        assert (sel[b, :, n:] == -1).all()
+    d = (so.float() - fo.float()).abs().max().item()
+    assert d <= (1e-5 if w.dtype == "f32" else 1e-2)
+    assert (sl - fl).abs().max().item() <= 1e-4
+
+
+def test_incremental_steps_hetero(vx):
+    """Appending one token per request per step, with centroids updated only
+    for the pages each step completes, matches the oracle at the first and
+    last step, and the incremental table equals a bulk rebuild bit for bit."""
+    c, _ = _prepared(vx, "hetero_small")
+    w = c.w
+    for s in range(w.steps):
+        H.set_step(c, s)
+        if s > 0:
+            ids = synth.completed_pages(c.layout, s)
+            if len(ids):
+                vx.centroid_update(c.kv, torch.from_numpy(ids).cuda())
+        if s in (0, w.steps - 1):
+            H.fix_gaps(c, range(w.batch))
+        q = c.q_host.cuda()
+        sel = H.run_indexer(vx, c, q)
+        out, lse = H.run_sparse(vx, c, q, sel)
+        if s in (0, w.steps - 1):
+            torch.cuda.synchronize()
+            for b in range(w.batch):
+                _check_request(vx, c, b, sel, out, lse)
+    inc = c.cent.clone()
+    c.cent.zero_()
+    L = synth.step_seq_lens(c.layout, w.steps - 1)
+    ids = np.concatenate([c.layout.page_table[b, :L[b] // w.page_size] for b in range(w.batch)])
+    vx.centroid_update(c.kv, torch.from_numpy(ids.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(ids.astype(np.int64)).cuda()
+    assert torch.equal(inc[idx], c.cent[idx])
+
+
+
+
+@pytest.mark.parametrize("dtype,D,G,S", [
+    ("f32", 64, 1, 16), ("bf16", 128, 1, 16), ("bf16", 64, 4, 16), ("f32", 128, 8, 16),
+    ("bf16", 128, 2, 64), ("bf16", 128, 8, 16)])
+@pytest.mark.parametrize("topk,bos,eos", [(4, 1, 1), (0, 1, 1), (3, 0, 2), (2, 2, 1)])
+def test_edge_lengths(vx, dtype, D, G, S, topk, bos, eos):
+    lens = (1, S - 1, S, S + 1, S * 6, S * 6 + 1, S * 9 + 3)
+    w = synth.Workload(name="edges", batch=len(lens), num_q_heads=2 * G, num_kv_heads=2,
+                       head_dim_qk=D, head_dim_v=D, page_size=S, dtype=dtype, topk=topk,
+                       structure="page_offset", seed=77, seq_lens=lens, n_bos=bos, n_eos=eos,
+                       spare_pages=5)
+    H.log(f"case {H.describe(w)} lens={lens} bos={bos} eos={eos}")
+    c = H.setup_case(vx, w)
+    H.build_centroids(vx, c)
+    H.fix_gaps(c, range(w.batch))
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    out, lse = H.run_sparse(vx, c, q, sel)
+    fo, fl = H.run_full(vx, c, q)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel, out, lse)
+        _check_request(vx, c, b, None, fo, fl, sparse=False)
+        if lens[b] == 1:       # one token: output is that token's value
+            v = H.to_f64(c.V[c.layout.page_table[b, 0], :, 0])          # [H_kv, D]
+            want = np.repeat(v, G, axis=0)
+            assert np.allclose(H.to_f64(out[b]), want, rtol=0, atol=1e-6 if dtype == "f32" else 1e-2)
+
+
+def test_empty_batch_is_a_no_op(vx):
+    w = synth.SMALL_WORKLOADS["qwen3_small"]
+    c = H.setup_case(vx, w)
+    bt = vx.Batch(page_table=c.pt[:0], seq_lens=c.seq_lens[:0], num_q_heads=w.num_q_heads,
+                  max_seq_len=4096)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    q = c.q_host.cuda()
+    sel = torch.empty((0, w.num_kv_heads, w.k_tot), dtype=torch.int32, device="cuda")
+    vx.score_topk(c.kv, bt, q, w.topk, 1, 1, sel, ws)
+    out = torch.empty((0, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype, device="cuda")
+    vx.sparse_paged_decode(c.kv, bt, q, sel, w.sm_scale, out, None, ws)
+    vx.full_paged_decode(c.kv, bt, q, w.sm_scale, out, None, ws)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- full size
+FULL = ["tiny_b1_l1k_f32", "qwen3_0p6b_b32_l32k", "long_b8_l128k", "mla_b64_l32k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(vx, name):
+    w = synth.get_workload(name)
+    _mla_guard(vx, w)
+    reqs = H.sample_requests(w.batch)
+    c, _ = _prepared(vx, name, reqs)
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    out, lse = H.run_sparse(vx, c, q, sel)
+    fo, fl = H.run_full(vx, c, q)
+    torch.cuda.synchronize()
+    H.assert_centroids(c, c.layout.page_table[reqs[0], :4])
+    for b in reqs:
+        H.log(f"  request {b}")
+        _check_request(vx, c, b, sel, out, lse)
+        _check_request(vx, c, b, None, fo, fl, sparse=False)
+    # every selection in the batch is a valid set: reserved pages present,
+    # ascending, -1 padded, size min(n_b, k_tot)
+    s = sel.cpu().numpy()
+    for b in range(w.batch):
+        n = c.n_pages(b)
+        for h in range(w.num_kv_heads):
+            row = s[b, h]
+            m = min(n, w.k_tot)
+            assert (row[m:] == -1).all() and np.all(np.diff(row[:m]) > 0)
+            assert set(orc.reserved_pages(n, w.n_bos, w.n_eos).tolist()) <= set(row[:m].tolist())
+
+
+def test_full_size_hetero_sampled(vx):
+    name = "hetero_b128_l4k_64k"
+    w = synth.get_workload(name)
+    reqs = H.sample_requests(w.batch)
+    c, _ = _prepared(vx, name, reqs)
+    for s in range(w.steps):
+        H.set_step(c, s)
+        if s > 0:
+            ids = synth.completed_pages(c.layout, s)
+            if len(ids):
+                vx.centroid_update(c.kv, torch.from_numpy(ids).cuda())
+        last = s == w.steps - 1
+        if last:
+            H.fix_gaps(c, reqs)
+        q = c.q_host.cuda()
+        sel = H.run_indexer(vx, c, q)
+        out, lse = H.run_sparse(vx, c, q, sel)
+    fo, fl = H.run_full(vx, c, q)
+    torch.cuda.synchronize()
+    for b in reqs:
+        H.log(f"  request {b}")
+        _check_request(vx, c, b, sel, out, lse)
+        _check_request(vx, c, b, None, fo, fl, sparse=False)
