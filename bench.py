@@ -161,7 +161,7 @@ def main():
     pool_bytes = lay.num_pages * w.num_kv_heads * w.page_size * w.elem_bytes * (
         w.head_dim_qk + (0 if w.v_aliases_k else w.head_dim_v))
     n_layers = args.layers or max(2, math.ceil(3 * MALL_BYTES / mean_step_bytes) + 1)
-    n_layers = max(1, min(n_layers, int((48 << 30) // max(pool_bytes, 1))))
+    n_layers = max(1, min(n_layers, 16, int((48 << 30) // max(pool_bytes, 1))))
     log(f"step bytes {mean_step_bytes / 1e6:.1f} MB, pool {pool_bytes / 1e9:.2f} GB, "
         f"{n_layers} layers")
 

@@ -28,7 +28,6 @@ constexpr int kMlaTargetBlocks = kNumCUs * 2;
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxCandidates = 16384;
 constexpr size_t kAlign = 256;
-constexpr bool kMlaAvailable = false;   // the MLA decode kernel is not built yet
 
 int g_pages_per_split_override = 0;
 
@@ -51,7 +50,6 @@ vx_status check_kv(const vx_paged_kv* kv) {
   if (kv->page_size != 16 && kv->page_size != 64) return VX_ERR_UNSUPPORTED;
   const int dq = kv->head_dim_qk, dv = kv->head_dim_v;
   if (dq == 576) {
-    if (!kMlaAvailable) return VX_ERR_UNSUPPORTED;
     if (kv->dtype != VX_BF16 || dv != 512 || !kv->v_aliases_k || kv->num_kv_heads != 1 ||
         kv->page_size != 64)
       return VX_ERR_UNSUPPORTED;
@@ -119,6 +117,7 @@ DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, boo
       ++pps;
   }
   pps = std::max(pps, ceil_div(pages, kMaxSplits));
+  if (is_mla(kv)) pps = std::min(pps, mla_max_pages_per_split());   // LDS page list
   p.pages_per_split = pps;
   p.n_split = ceil_div(pages, pps);
   if (p.n_split > 1) {

@@ -68,6 +68,7 @@ hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s);
 // D = D_qk = D_v for this path; G = H_q / H_kv.
 hipError_t launch_decode_valu(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
+int mla_max_pages_per_split();
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
 
 }  // namespace vx

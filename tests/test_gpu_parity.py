@@ -150,9 +150,11 @@ def test_sparse_equals_full_when_topk_covers_all(vx, name):
         n = c.n_pages(b)
         assert sel[b, :, :n].cpu().tolist() == [list(range(n))] * w.num_kv_heads
         assert (sel[b, :, n:] == -1).all()
+    # the two calls plan different splits, so only fp32 (and, for MLA, bf16
+    # probability) rounding separates them
     d = (so.float() - fo.float()).abs().max().item()
     assert d <= (1e-5 if w.dtype == "f32" else 1e-2)
-    assert (sl - fl).abs().max().item() <= 1e-4
+    assert (sl - fl).abs().max().item() <= (1e-5 if w.dtype == "f32" else 1e-3)
 
 
 def test_incremental_steps_hetero(vx):
