@@ -22,11 +22,15 @@ namespace {
 using namespace vx;
 
 constexpr int kNumCUs = 256;                    // MI355X
-constexpr int kSparseTargetWaves = kNumCUs * 8;
-constexpr int kFullTargetWaves = kNumCUs * 32;
+// blocks per launch the planner aims for (VALU decode blocks are 8 waves,
+// MLA blocks 4): one wave of resident blocks for the sparse step, several
+// for the long dense stream so that unequal requests even out
+constexpr int kSparseTargetBlocks = kNumCUs;
+constexpr int kFullTargetBlocks = kNumCUs * 16;
 constexpr int kMlaTargetBlocks = kNumCUs * 2;
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxCandidates = 16384;
+constexpr int kFusedMaxPages = 6144;            // page ids + keys in LDS: 48 KiB
 constexpr size_t kAlign = 256;
 
 int g_pages_per_split_override = 0;
@@ -106,10 +110,10 @@ DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, boo
            (double)ceil_div(pages, pps) * G * (kv->head_dim_v + 2) * 8 > 0.25 * kv_bytes)
       ++pps;
   } else {
-    const int target = sparse ? kSparseTargetWaves : kFullTargetWaves;
+    const int target = sparse ? kSparseTargetBlocks : kFullTargetBlocks;
     const int n_want = std::max(1, ceil_div(target, units));
     pps = ceil_div(pages, n_want);
-    if (!sparse) pps = std::max(pps, 16);
+    if (!sparse) pps = std::max(pps, 64);
     const double kv_bytes = (double)pages * kv->page_size *
                             (kv->head_dim_qk + kv->head_dim_v) * elem_bytes(kv->dtype);
     while (ceil_div(pages, pps) > 1 &&
@@ -230,8 +234,45 @@ vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void
   const int max_tokens = batch->max_seq_len;
   float* scores = reinterpret_cast<float*>(workspace);
   const int max_cand = std::max(mp - n_bos - n_eos, 0);
-
   const bool need_scores = max_cand > topk && topk > 0;   // else all or none are taken
+
+  TopkArgs t{};
+  t.scores = scores;
+  t.seq_lens = batch->seq_lens;
+  t.sel = sel;
+  t.B = batch->batch;
+  t.H_kv = kv->num_kv_heads;
+  t.S_p = kv->page_size;
+  t.score_stride = mp;
+  t.max_tokens = max_tokens;
+  t.topk = topk;
+  t.n_bos = n_bos;
+  t.n_eos = n_eos;
+  t.k_tot = k_tot;
+
+  // One block per (request, KV head) when there are enough of them to fill
+  // the GPU (or the whole problem is tiny) and the candidate keys fit in LDS.
+  const long long units = (long long)batch->batch * kv->num_kv_heads;
+  if (fused_indexer_supported(kv->dtype, kv->head_dim_qk) && mp <= kFusedMaxPages &&
+      (units >= kNumCUs / 2 || units * mp <= 4096)) {
+    ScoreArgs s{};
+    s.q = q;
+    s.cent = kv->centroids;
+    s.pt = batch->page_table;
+    s.seq_lens = batch->seq_lens;
+    s.B = batch->batch;
+    s.H_q = batch->num_q_heads;
+    s.H_kv = kv->num_kv_heads;
+    s.D = kv->head_dim_qk;
+    s.S_p = kv->page_size;
+    s.pt_stride = batch->max_pages_per_req;
+    s.score_stride = mp;
+    s.max_tokens = max_tokens;
+    s.n_bos = n_bos;
+    s.n_eos = n_eos;
+    return hip_status(launch_indexer_fused(kv->dtype, s, t, stream));
+  }
+
   if (need_scores) {
     ScoreArgs s{};
     s.q = q;
@@ -249,26 +290,15 @@ vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void
     s.max_tokens = max_tokens;
     s.n_bos = n_bos;
     s.n_eos = n_eos;
+    // about one block per CU per 4 waves' worth of in-flight loads: 64
+    // candidates (all KV heads) per block, more when the batch is large
     const long long total = (long long)batch->batch * max_cand;
-    int cpb = ceil_div(total, 1024);
-    cpb = std::min(std::max(cpb, 16), 256);
+    int cpb = ceil_div(total, 2048);
+    cpb = std::min(std::max(cpb, 32), 256);
     s.cand_per_block = cpb;
     hipError_t e = launch_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
     if (e != hipSuccess) return VX_ERR_HIP;
   }
-  TopkArgs t{};
-  t.scores = scores;
-  t.seq_lens = batch->seq_lens;
-  t.sel = sel;
-  t.B = batch->batch;
-  t.H_kv = kv->num_kv_heads;
-  t.S_p = kv->page_size;
-  t.score_stride = mp;
-  t.max_tokens = max_tokens;
-  t.topk = topk;
-  t.n_bos = n_bos;
-  t.n_eos = n_eos;
-  t.k_tot = k_tot;
   return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
 }
 

@@ -3,67 +3,80 @@
 // vortex_torch README's "Quick Example" reduces a finished page's keys with a
 // mean over its token rows into a centroid cache).
 //
-// One wave per (listed page, KV head).  The page-head tile is S_p rows of
-// D elements, contiguous in HBM (S_p * D * e bytes: 4 KiB for 16 x 128 bf16).
-// Lanes read 16-byte segments so each wave-load covers 1 KiB contiguously;
-// column sums are kept in fp32 per lane, merged across lane groups with
-// shuffles, scaled by 1/S_p (exact: S_p is a power of two) and rounded once.
+// One block per (listed page, KV head).  The page-head tile is S_p rows of
+// D elements, contiguous in HBM (4 KiB for 16 x 128 bf16, 72 KiB for an MLA
+// page).  Thread t reads 16-byte segment t % SEGS of rows t / SEGS,
+// t / SEGS + RG, ..., all issued before the first is used, keeping fp32 sums;
+// the RG row groups are then added in a fixed order through LDS, scaled by
+// 1/S_p (exact: S_p is a power of two) and rounded once.
 #include "vx_device.h"
 #include "vx_internal.h"
 
 namespace vx {
 namespace {
 
-template <typename T, int D>
-__global__ __launch_bounds__(64) void centroid_kernel(CentroidArgs a) {
-  using V = Vec16<T>;
-  constexpr int E = V::E;
-  constexpr int SEGS = D / E;               // 16-byte segments per row
-  const int lane = threadIdx.x;
-  const int i = blockIdx.x, h = blockIdx.y;
-  const int page = a.ids[i];
-  const size_t tile = ((size_t)page * a.H_kv + h) * (size_t)a.S_p * D;
-  const T* kp = reinterpret_cast<const T*>(a.k) + tile;
-  T* cp = reinterpret_cast<T*>(a.cent) + ((size_t)page * a.H_kv + h) * D;
-  const float inv = 1.0f / (float)a.S_p;
+constexpr int kMaxRowsPerThread = 8;
 
-  if constexpr (SEGS <= 64) {
-    constexpr int R = 64 / SEGS;            // rows per wave-load
-    const int seg = lane % SEGS, grp = lane / SEGS;
-    float acc[E];
+template <typename T, int D>
+struct CentroidShape {
+  static constexpr int E = Vec16<T>::E;
+  static constexpr int SEGS = D / E;                       // 16-byte segments per row
+  static constexpr int RG = (SEGS * 16 <= 1024) ? 16 : 1024 / SEGS;   // row groups
+  static constexpr int THREADS = SEGS * RG;
+};
+
+template <typename T, int D, int NT>
+__global__ __launch_bounds__(NT) void centroid_kernel(CentroidArgs a) {
+  using V = Vec16<T>;
+  using S = CentroidShape<T, D>;
+  constexpr int E = S::E, SEGS = S::SEGS, RG = S::RG;
+  __shared__ float red[RG][SEGS * E];
+  const int tid = threadIdx.x;
+  const int seg = tid % SEGS, rg = tid / SEGS;
+  const int page = a.ids[blockIdx.x], h = blockIdx.y;
+  const T* kp = reinterpret_cast<const T*>(a.k) + ((size_t)page * a.H_kv + h) * (size_t)a.S_p * D;
+
+  uint4 buf[kMaxRowsPerThread];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int t = grp; t < a.S_p; t += R) {
+  for (int j = 0; j < kMaxRowsPerThread; ++j) {
+    const int t = rg + j * RG;
+    if (t < a.S_p) buf[j] = ld16(kp + (size_t)t * D + seg * E);
+  }
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxRowsPerThread; ++j) {
+    if (rg + j * RG < a.S_p) {
       float f[E];
-      V::unpack(ld16(kp + (size_t)t * D + seg * E), f);
+      V::unpack(buf[j], f);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] += f[e];
     }
+  }
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = across_groups_sum<SEGS>(acc[e]) * inv;
-    if (grp == 0) st16(cp + seg * E, V::pack(acc));
-  } else {
-    for (int seg = lane; seg < SEGS; seg += 64) {
-      float acc[E];
+  for (int e = 0; e < E; ++e) red[rg][seg * E + e] = acc[e];
+  __syncthreads();
+  if (tid < SEGS) {
+    const float inv = 1.0f / (float)a.S_p;
+    float sum[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = 0.f;
-      for (int t = 0; t < a.S_p; ++t) {
-        float f[E];
-        V::unpack(ld16(kp + (size_t)t * D + seg * E), f);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += f[e];
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] *= inv;
-      st16(cp + seg * E, V::pack(acc));
+    for (int e = 0; e < E; ++e) {
+      float x = 0.f;
+      for (int g = 0; g < RG; ++g) x += red[g][tid * E + e];
+      sum[e] = x * inv;
     }
+    T* cp = reinterpret_cast<T*>(a.cent) + ((size_t)page * a.H_kv + h) * D;
+    st16(cp + tid * E, V::pack(sum));
   }
 }
 
 template <typename T, int D>
 hipError_t run(const CentroidArgs& a, hipStream_t s) {
-  dim3 grid(a.n_ids, a.H_kv);
-  hipLaunchKernelGGL((centroid_kernel<T, D>), grid, dim3(64), 0, s, a);
+  using S = CentroidShape<T, D>;
+  if (a.S_p > S::RG * kMaxRowsPerThread) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((centroid_kernel<T, D, S::THREADS>), dim3(a.n_ids, a.H_kv), dim3(S::THREADS),
+                     0, s, a);
   return hipGetLastError();
 }
 

@@ -57,6 +57,37 @@ template <> struct Vec16<bf16_t> {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// ---------------------------------------------------------------- DPP
+// Data-parallel-primitive lane moves (VALU, no LDS traffic).  Controls:
+// quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), [2,3,0,1] = 0x4E (lane ^ 2),
+// row_half_mirror = 0x141 (i <-> 7-i within 8), row_mirror = 0x140
+// (i <-> 15-i within 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W in {1, 2, 4, 8, 16}), every lane of
+// the group receiving the total.
+template <int W>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (W >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (W >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (W >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (W >= 16) x += dpp_mov<0x140>(x);
+  return x;
+}
+
+// Sum over aligned groups of W lanes for any power of two W <= 64.
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  x = row_sum<(W < 16 ? W : 16)>(x);
+  if constexpr (W >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
 // ---------------------------------------------------------------- reductions
 // All-reduce over aligned groups of W consecutive lanes (W a power of two).
 template <int W>

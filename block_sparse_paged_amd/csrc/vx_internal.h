@@ -65,6 +65,9 @@ struct CombineArgs {
 hipError_t launch_centroid(int dtype, const CentroidArgs& a, hipStream_t s);
 hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s);
+// One block per (request, KV head) scores and selects (rows of <= 64 lanes).
+bool fused_indexer_supported(int dtype, int D);
+hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s);
 // D = D_qk = D_v for this path; G = H_q / H_kv.
 hipError_t launch_decode_valu(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);

@@ -4,18 +4,26 @@
 // structure; "Using Your Sparse Attention with SGLang": reserved first / last
 // pages and the top-k value).
 //
-// K2 score_kernel  - grid (candidate chunks, B), 4 waves per block.  The
-//   group-mean queries of all KV heads of the request sit in LDS (fp32).
-//   Centroid rows are gathered through the page table; for one page the H_kv
-//   rows are contiguous (H_kv * D * e bytes), so a wave-load of 16 bytes per
-//   lane reads 1 KiB of consecutive heads.  Each (page, head) dot product is
-//   reduced across the lanes holding that row.  Scores go to the workspace
-//   indexed by candidate number.
-// K3 topk_kernel   - one 256-thread block per (request, KV head).  Scores are
-//   mapped to order-preserving uint32 keys in LDS, the k-th largest key is
-//   found by a 4-pass 8-bit radix select (LDS histograms), keys equal to the
-//   threshold are taken lowest-index first via a block-wide scan, and the
-//   union with the reserved pages is compacted in ascending page order.
+// Two schedules, chosen by the host planner:
+//
+// fused   one 512-thread block per (request, KV head) scores every candidate
+//         page of that head and selects in the same block: the page table
+//         slice is staged in LDS, each wave keeps 16 centroid-row loads in
+//         flight, scores become order-preserving keys in LDS, and no score
+//         touches HBM.  Used when there are enough (request, KV head) units
+//         to fill the GPU and the candidate keys fit in LDS.
+// split   K2 score_kernel: blocks over (candidate chunk, request) score all
+//         KV heads of their pages (the H_kv rows of a page are contiguous, so
+//         a wave-load reads 1 KiB of consecutive heads) into the workspace;
+//         K3 topk_kernel: one block per (request, KV head) selects.  Used when
+//         few (request, KV head) units exist (long contexts, MLA's single
+//         latent head).
+//
+// Selection (both schedules): exact top-k by an 8-bit radix select over the
+// keys (one LDS histogram per pass, every wave locating the digit itself, and
+// an early stop once the boundary bin is taken whole), equal keys ranked by
+// page, then the union with the reserved pages is compacted in ascending
+// page order with one block-wide scan.
 #include "vx_device.h"
 #include "vx_internal.h"
 
@@ -24,12 +32,199 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kTopkThreads = 256;
+constexpr int kFusedThreads = 512;
+constexpr int kLoadsInFlight = 16;   // wave-loads issued before the first is used
 
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 and +0 are equal
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan of one int per thread over an NT-thread block, in thread
+// order.  `tmp` holds NT/64 ints of LDS.  Also returns the block total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int inc = wave_inclusive_scan(x);
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = tmp[w];
+    base += (w < wave) ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - x;
+}
+
+// Selects and writes one (request, KV head) row of `sel`.
+//   keys     LDS, n_cand order-preserving keys of candidates n_bos.. (in page order)
+//   hist     LDS, 4*256 ints, zero on entry
+// Keys and the zeroed histograms must be visible to every thread (the caller
+// synchronises first).
+template <int NT>
+__device__ void select_pages(const uint32_t* keys, int n_cand, int n_b, int topk, int n_bos,
+                             int n_eos, int k_tot, int32_t* out, int* hist, int* scan_tmp) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool all = n_cand <= topk;
+  const bool none = !all && topk == 0;
+  uint32_t thr = 0, msk = 0;
+  int take_eq = 0, cnt_eq = 0;
+  if (!all && !none) {
+    int remaining = topk;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      int* H = hist + 256 * pass;
+      for (int i = tid; i < n_cand; i += NT) {
+        const uint32_t k = keys[i];
+        if ((k & msk) == thr) atomicAdd(&H[(k >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      // every wave finds the bin where the count from the top crosses `remaining`
+      const int h0 = H[4 * lane], h1 = H[4 * lane + 1], h2 = H[4 * lane + 2], h3 = H[4 * lane + 3];
+      const int own = h0 + h1 + h2 + h3;
+      int suf = own;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_down(suf, d, 64);
+        if (lane + d < 64) suf += y;
+      }
+      int acc = suf - own, dsel = -1, above = 0, cnt = 0;
+      if (acc < remaining && acc + h3 >= remaining) { dsel = 4 * lane + 3; above = acc; cnt = h3; }
+      acc += h3;
+      if (dsel < 0 && acc < remaining && acc + h2 >= remaining) { dsel = 4 * lane + 2; above = acc; cnt = h2; }
+      acc += h2;
+      if (dsel < 0 && acc < remaining && acc + h1 >= remaining) { dsel = 4 * lane + 1; above = acc; cnt = h1; }
+      acc += h1;
+      if (dsel < 0 && acc < remaining && acc + h0 >= remaining) { dsel = 4 * lane; above = acc; cnt = h0; }
+      const unsigned long long found = __ballot(dsel >= 0);
+      const int src = __builtin_ctzll(found);
+      const int d = __builtin_amdgcn_readlane(dsel, src);
+      above = __builtin_amdgcn_readlane(above, src);
+      cnt = __builtin_amdgcn_readlane(cnt, src);
+      remaining -= above;
+      thr |= (uint32_t)d << shift;
+      msk |= 0xFFu << shift;
+      cnt_eq = cnt;
+      if (remaining == cnt) break;    // the whole boundary bin is taken
+    }
+    take_eq = remaining;
+  }
+  const bool need_rank = !all && !none && take_eq < cnt_eq;
+
+  // thread tid owns logical pages [p_lo, p_hi)
+  const int per = (n_b + NT - 1) / NT;
+  const int p_lo = min(tid * per, n_b), p_hi = min(p_lo + per, n_b);
+  const int eos_lo = n_b - n_eos;
+  int eq_rank = 0, dummy;
+  if (need_rank) {
+    int n_eq = 0;
+    for (int p = max(p_lo, n_bos); p < min(p_hi, eos_lo); ++p) n_eq += (keys[p - n_bos] & msk) == thr;
+    eq_rank = block_exclusive_scan<NT>(n_eq, scan_tmp, &dummy);
+  }
+  auto take = [&](int p, int& rank) -> bool {
+    if (p < n_bos || p >= eos_lo) return true;
+    if (all || none) return all;
+    const uint32_t km = keys[p - n_bos] & msk;
+    bool t = km > thr;
+    if (km == thr) {
+      t = !need_rank || rank < take_eq;
+      ++rank;
+    }
+    return t;
+  };
+  int r = eq_rank, n_take = 0;
+  for (int p = p_lo; p < p_hi; ++p) n_take += take(p, r) ? 1 : 0;
+  int total;
+  int pos = block_exclusive_scan<NT>(n_take, scan_tmp, &total);
+  r = eq_rank;
+  for (int p = p_lo; p < p_hi; ++p)
+    if (take(p, r)) out[pos++] = p;
+  for (int i = total + tid; i < k_tot; i += NT) out[i] = -1;
+}
+
+// ---------------------------------------------------------------- fused
+template <typename T, int D>
+__global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs a, TopkArgs t) {
+  using V = Vec16<T>;
+  constexpr int E = V::E;
+  constexpr int LH = D / E;                  // lanes per centroid row
+  constexpr int R = 64 / LH;                 // rows per wave-load
+  constexpr int NW = kFusedThreads / 64;
+  constexpr int U = kLoadsInFlight;
+  static_assert(LH * R == 64, "fused indexer needs rows of at most 64 lanes");
+  extern __shared__ uint32_t dyn[];          // phys [max_cand] then keys [max_cand]
+  __shared__ float qbar[D];
+  __shared__ int hist[4 * 256];
+  __shared__ int scan_tmp[NW];
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int seg = lane % LH, grp = lane / LH;
+  int seq = a.seq_lens[b];
+  seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
+  const int n_b = (seq + a.S_p - 1) / a.S_p;
+  const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
+  const bool scoring = n_cand > t.topk && t.topk > 0;
+  int32_t* phys = reinterpret_cast<int32_t*>(dyn);
+  uint32_t* keys = dyn + a.score_stride;
+
+  if (scoring) {
+    const int G = a.H_q / a.H_kv;
+    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.H_q + (size_t)h * G) * D;
+    for (int d = tid; d < D; d += kFusedThreads) {
+      float s = 0.f;
+      for (int g = 0; g < G; ++g) s += V::to_f32(qb[(size_t)g * D + d]);
+      qbar[d] = s * (1.0f / (float)G);
+    }
+    const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
+    for (int i = tid; i < n_cand; i += kFusedThreads) phys[i] = ptb[i];
+  }
+  for (int i = tid; i < 4 * 256; i += kFusedThreads) hist[i] = 0;
+  __syncthreads();
+
+  if (scoring) {
+    float qr[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) qr[e] = qbar[seg * E + e];
+    const T* cent = reinterpret_cast<const T*>(a.cent);
+    constexpr int STEP = NW * R;               // rows per block-wide wave-load
+    for (int r0 = w * R; r0 < n_cand; r0 += STEP * U) {
+      uint4 buf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = r0 + u * STEP + grp;
+        buf[u] = c < n_cand ? ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + seg * E)
+                            : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = r0 + u * STEP + grp;
+        float f[E];
+        V::unpack(buf[u], f);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc = fmaf(qr[e], f[e], acc);
+        acc = lane_group_sum<LH>(acc);
+        if (seg == 0 && c < n_cand) keys[c] = order_key(acc);
+      }
+    }
+  }
+  __syncthreads();
+  select_pages<kFusedThreads>(keys, n_cand, n_b, t.topk, t.n_bos, t.n_eos, t.k_tot,
+                              t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, hist, scan_tmp);
+}
+
+// ---------------------------------------------------------------- split
 template <typename T, int D>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   using V = Vec16<T>;
   constexpr int E = V::E;
   constexpr int LH = D / E;                 // 16-byte segments per centroid row
+  constexpr int U = kLoadsInFlight;
   extern __shared__ float smem[];           // qbar [H_kv][D] then phys ids
   float* qbar = smem;
   int32_t* phys = reinterpret_cast<int32_t*>(smem + a.H_kv * D);
@@ -66,84 +261,95 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 
   if constexpr (LH <= 64) {
     constexpr int R = 64 / LH;              // rows per wave-load
-    constexpr int U = 4;                    // wave-loads in flight
+    constexpr int STEP = (kScoreThreads / 64) * R;
     const int seg = lane % LH, grp = lane / LH;
-    const int step = 4 * R;                 // rows advanced per wave-load by the block
-    for (int r0 = wave * R; r0 < rows; r0 += step * U) {
+    for (int r0 = wave * R; r0 < rows; r0 += STEP * U) {
       uint4 buf[U];
-      int rr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * step + grp;
-        rr[u] = r;
+        const int r = r0 + u * STEP + grp;
         if (r < rows) {
           const int c = r / a.H_kv, h = r - c * a.H_kv;
           buf[u] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + seg * E);
+        } else {
+          buf[u] = make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int r = rr[u];
+        const int r = r0 + u * STEP + grp;
         const int rc = r < rows ? r : 0;
         const int c = rc / a.H_kv, h = rc - c * a.H_kv;
         float f[E];
-        V::unpack(r < rows ? buf[u] : make_uint4(0, 0, 0, 0), f);
+        V::unpack(buf[u], f);
         const float* qh = qbar + h * D + seg * E;
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc = fmaf(qh[e], f[e], acc);
-        acc = group_sum<LH>(acc);
+        acc = lane_group_sum<LH>(acc);
         if (seg == 0 && r < rows) out[(size_t)h * a.score_stride + c0 + c] = acc;
       }
     }
   } else {
-    // rows wider than a wave (MLA): one row per wave-step, full-wave reduce
-    for (int r = wave; r < rows; r += 4) {
-      const int c = r / a.H_kv, h = r - c * a.H_kv;
-      const T* row = cent + ((size_t)phys[c] * a.H_kv + h) * D;
-      const float* qh = qbar + h * D;
-      float acc = 0.f;
-      for (int seg = lane; seg < LH; seg += 64) {
-        float f[E];
-        V::unpack(ld16(row + seg * E), f);
+    // Rows of more than 64 segments (MLA: 72).  Eight rows form a tile of
+    // 9 wave-loads: eight "head" loads of segments 0..63 of one row each and
+    // one "tail" load of segments 64..71 of all eight rows.
+    static_assert(LH > 64 && LH <= 72, "row width");
+    constexpr int TL = LH - 64;             // tail segments per row (8)
+    constexpr int RT = 64 / TL;             // rows per tile (8)
+    for (int r0 = wave * RT; r0 < rows; r0 += 4 * RT) {
+      uint4 hb[RT], tb;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc = fmaf(qh[seg * E + e], f[e], acc);
+      for (int i = 0; i < RT; ++i) {
+        const int r = r0 + i;
+        if (r < rows) {
+          const int c = r / a.H_kv, h = r - c * a.H_kv;
+          hb[i] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + lane * E);
+        } else {
+          hb[i] = make_uint4(0, 0, 0, 0);
+        }
       }
-      acc = wave_sum(acc);
-      if (lane == 0) out[(size_t)h * a.score_stride + c0 + c] = acc;
+      const int tr = r0 + lane / TL, tseg = 64 + lane % TL;
+      if (tr < rows) {
+        const int c = tr / a.H_kv, h = tr - c * a.H_kv;
+        tb = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + tseg * E);
+      } else {
+        tb = make_uint4(0, 0, 0, 0);
+      }
+      float tp;
+      {
+        const int c = (tr < rows ? tr : 0) / a.H_kv, h = (tr < rows ? tr : 0) - c * a.H_kv;
+        float f[E];
+        V::unpack(tb, f);
+        const float* qh = qbar + h * D + tseg * E;
+        tp = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) tp = fmaf(qh[e], f[e], tp);
+        tp = row_sum<TL>(tp);               // sum over the TL lanes of one row
+      }
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int r = r0 + i;
+        const int rc = r < rows ? r : 0;
+        const int c = rc / a.H_kv, h = rc - c * a.H_kv;
+        float f[E];
+        V::unpack(hb[i], f);
+        const float* qh = qbar + h * D + lane * E;
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc = fmaf(qh[e], f[e], acc);
+        acc = lane_group_sum<64>(acc) +
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tp), i * TL));
+        if (lane == 0 && r < rows) out[(size_t)h * a.score_stride + c0 + c] = acc;
+      }
     }
   }
 }
 
-// Exclusive scan of one int per thread over a 256-thread block, in thread
-// order.  `tmp` holds at least 4 ints of LDS.  Returns the block total too.
-__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int inc = wave_inclusive_scan(x);
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
-    const int t = tmp[w];
-    base += (w < wave) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + inc - x;
-}
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 and +0 are equal
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   extern __shared__ uint32_t keys[];        // [n_cand]
-  __shared__ int hist[256];
-  __shared__ int scan_tmp[4];
-  __shared__ int pick[2];
+  __shared__ int hist[4 * 256];
+  __shared__ int scan_tmp[kTopkThreads / 64];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;                // b * H_kv + h
@@ -152,107 +358,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
   const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
-  const bool all = n_cand <= a.topk;
-  int32_t* out = a.sel + (size_t)bh * a.k_tot;
-
-  uint32_t thr = 0xFFFFFFFFu;   // keys above thr are taken ...
-  int take_eq = 0;              // ... and the first take_eq keys equal to thr
-  const bool none = !all && a.topk == 0;
-  if (!all && !none) {
+  if (n_cand > a.topk && a.topk > 0) {
     const float* sc = a.scores + (size_t)bh * a.score_stride;
     for (int i = tid; i < n_cand; i += kTopkThreads) keys[i] = order_key(sc[i]);
-    uint32_t prefix = 0, mask = 0;
-    int remaining = a.topk;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n_cand; i += kTopkThreads) {
-        const uint32_t k = keys[i];
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l owns bins 4l..4l+3; count keys in bins above each bin
-        const int h0 = hist[4 * tid], h1 = hist[4 * tid + 1];
-        const int h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
-        const int own = h0 + h1 + h2 + h3;
-        // exclusive suffix sum over lanes (higher lanes hold higher bins)
-        int suf = own;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_down(suf, d, 64);
-          if (tid + d < 64) suf += y;
-        }
-        int above = suf - own;              // keys in bins of higher lanes
-        int digit = -1, above_d = 0;
-        if (above + h3 >= remaining && above < remaining) { digit = 4 * tid + 3; above_d = above; }
-        above += h3;
-        if (digit < 0 && above + h2 >= remaining && above < remaining) { digit = 4 * tid + 2; above_d = above; }
-        above += h2;
-        if (digit < 0 && above + h1 >= remaining && above < remaining) { digit = 4 * tid + 1; above_d = above; }
-        above += h1;
-        if (digit < 0 && above + h0 >= remaining && above < remaining) { digit = 4 * tid; above_d = above; }
-        if (digit >= 0) { pick[0] = digit; pick[1] = above_d; }
-      }
-      __syncthreads();
-      prefix |= (uint32_t)pick[0] << shift;
-      mask |= 0xFFu << shift;
-      remaining -= pick[1];
-      __syncthreads();
-    }
-    thr = prefix;
-    take_eq = remaining;
   }
-
-  // Thread tid owns logical pages [tid*per, tid*per + per).
-  const int per = (n_b + kTopkThreads - 1) / kTopkThreads;
-  const int p_lo = min(tid * per, n_b), p_hi = min(p_lo + per, n_b);
-  // rank of equal-to-threshold candidates, in page order
-  int n_eq = 0;
-  if (!all && !none) {
-    for (int p = p_lo; p < p_hi; ++p) {
-      const int c = p - a.n_bos;
-      if (c >= 0 && c < n_cand && keys[c] == thr) ++n_eq;
-    }
-  }
-  int dummy;
-  int eq_rank = block_exclusive_scan(n_eq, scan_tmp, &dummy);
-  // which pages are taken, counted per thread
-  const int eos_lo = n_b - a.n_eos;
-  int n_take = 0;
-  for (int p = p_lo; p < p_hi; ++p) {
-    const int c = p - a.n_bos;
-    bool take;
-    if (p < a.n_bos || p >= eos_lo) {
-      take = true;
-    } else if (all || none) {
-      take = all;
-    } else {
-      const uint32_t k = keys[c];
-      take = k > thr || (k == thr && eq_rank < take_eq);
-      if (k == thr) ++eq_rank;
-    }
-    n_take += take ? 1 : 0;
-  }
-  int total;
-  int pos = block_exclusive_scan(n_take, scan_tmp, &total);
-  // second pass writes the taken pages (recomputing the same decisions)
-  eq_rank -= n_eq;
-  for (int p = p_lo; p < p_hi; ++p) {
-    const int c = p - a.n_bos;
-    bool take;
-    if (p < a.n_bos || p >= eos_lo) {
-      take = true;
-    } else if (all || none) {
-      take = all;
-    } else {
-      const uint32_t k = keys[c];
-      take = k > thr || (k == thr && eq_rank < take_eq);
-      if (k == thr) ++eq_rank;
-    }
-    if (take) out[pos++] = p;
-  }
-  for (int i = total + tid; i < a.k_tot; i += kTopkThreads) out[i] = -1;
+  for (int i = tid; i < 4 * 256; i += kTopkThreads) hist[i] = 0;
+  __syncthreads();
+  select_pages<kTopkThreads>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
+                             a.sel + (size_t)bh * a.k_tot, hist, scan_tmp);
 }
 
 template <typename T, int D>
@@ -262,7 +375,19 @@ hipError_t run_score(const ScoreArgs& a, int grid_x, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t run_fused(const ScoreArgs& a, const TopkArgs& t, hipStream_t s) {
+  const size_t lds = 2 * (size_t)(a.score_stride > 0 ? a.score_stride : 1) * sizeof(uint32_t);
+  hipLaunchKernelGGL((indexer_fused_kernel<T, D>), dim3(a.H_kv, a.B), dim3(kFusedThreads), lds, s,
+                     a, t);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool fused_indexer_supported(int dtype, int D) {
+  return (dtype == 0 && (D == 64 || D == 128)) || (dtype == 1 && (D == 64 || D == 128));
+}
 
 hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s) {
   if (dtype == 0) {
@@ -275,6 +400,21 @@ hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s
       case 64: return run_score<bf16_t, 64>(a, grid_x, s);
       case 128: return run_score<bf16_t, 128>(a, grid_x, s);
       case 576: return run_score<bf16_t, 576>(a, grid_x, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s) {
+  if (dtype == 0) {
+    switch (a.D) {
+      case 64: return run_fused<float, 64>(a, t, s);
+      case 128: return run_fused<float, 128>(a, t, s);
+    }
+  } else {
+    switch (a.D) {
+      case 64: return run_fused<bf16_t, 64>(a, t, s);
+      case 128: return run_fused<bf16_t, 128>(a, t, s);
     }
   }
   return hipErrorInvalidValue;
