@@ -1,15 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of block-top-k sparse paged decode on one MI355X.
 
-One step = one decode query per request through one attention layer: the
-centroid update for the pages this step's token completes, the indexer
-(group-mean query, centroid scores through the page table, exact top-k with
-the reserved first / last pages), and split-K attention over the selected
-pages.  Steps cycle over several independent layers (separate KV pools and
-centroid tables of the same shape), so a step's working set is not still
-sitting in the 256 MB on-package cache from the previous visit.  The dense
-paged decode over every page is timed afterwards on the same layers, for the
-speedup.  All inputs are synthetic and seeded.
+One step = one decode query per request through one attention layer, in one
+call of vx_sparse_decode_step: the centroid of the page this step's token
+completes, the indexer (group-mean query, centroid scores through the page
+table, exact top-k with the reserved first / last pages) and attention over
+the selected pages.  Steps cycle over several independent layers (separate
+KV pools and centroid tables of the same shape), so a step's working set is
+not still sitting in the 256 MB on-package cache from the previous visit.
+After the timed steps the same work is run once more as separate calls
+(vx_centroid_update, vx_score_topk, vx_sparse_paged_decode) for a per-stage
+breakdown, then the dense paged decode over every page for the speedup.  All
+inputs are synthetic and seeded.
 
 Prints one JSON line on stdout.  Progress goes to stderr.
 
@@ -131,6 +133,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized buffer a few times (reference for HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -146,6 +150,17 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.copy_calibration:
+        # a plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # per dispatch calibrate the counters used for the roofline's traffic
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
     vx.load_library()
     w = synth.get_workload(args.workload)
     lay = synth.build_layout(w)
@@ -190,24 +205,27 @@ def main():
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype, device=dev)
     lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
     kv0 = layers[0]["kv"]
+    ws_step = vx.alloc_workspace(vx.VX_OP_DECODE_STEP, kv0, batches[0], w.k_tot)
     ws_idx = vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, kv0, batches[0])
     ws_dec = vx.alloc_workspace(vx.VX_OP_SPARSE_DECODE, kv0, batches[0], w.k_tot)
     ws_full = vx.alloc_workspace(vx.VX_OP_FULL_DECODE, kv0, batches[0])
     stream = torch.cuda.current_stream()
 
-    # prepared calls per (layer, step-of-schedule)
+    # prepared calls per (layer, step of the schedule)
     calls = []
     for li, lay_i in enumerate(layers):
         per = []
         for s in range(T):
             kv, bt, q = lay_i["kv"], batches[s], lay_i["qs"][s]
+            c_step = vx.prepare_sparse_decode_step(kv, bt, q, w.topk, w.n_bos, w.n_eos, True,
+                                                   w.sm_scale, sel, out, lse, ws_step, stream)
             c_upd = (vx.prepare_centroid_update(kv, done_ids[s], stream)
                      if done_ids[s].numel() else None)
             c_idx = vx.prepare_score_topk(kv, bt, q, w.topk, w.n_bos, w.n_eos, sel, ws_idx, stream)
             c_dec = vx.prepare_sparse_paged_decode(kv, bt, q, sel, w.sm_scale, out, lse, ws_dec,
                                                    stream)
             c_full = vx.prepare_full_paged_decode(kv, bt, q, w.sm_scale, out, lse, ws_full, stream)
-            per.append((c_upd, c_idx, c_dec, c_full))
+            per.append({"step": c_step, "upd": c_upd, "idx": c_idx, "dec": c_dec, "full": c_full})
         calls.append(per)
 
     K_steps, W_steps = args.steps, args.warmup
@@ -216,68 +234,84 @@ def main():
     def schedule(i):
         return calls[i % nL][i % T]
 
-    # ---------------- sparse steps
+    # ---------------- timed sparse steps (fused entry point)
     for i in range(W_steps):
-        c_upd, c_idx, c_dec, _ = schedule(i)
-        if c_upd:
-            c_upd()
-        c_idx()
-        c_dec()
+        schedule(i)["step"]()
     torch.cuda.synchronize()
     log(f"warmup {W_steps} steps done")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K_steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K_steps):
-        c_upd, c_idx, c_dec, _ = schedule(W_steps + i)
-        e = ev[i]
-        e[0].record(stream)
-        if c_upd:
-            c_upd()
-        e[1].record(stream)
-        c_idx()
-        e[2].record(stream)
-        c_dec()
-        e[3].record(stream)
+        c = schedule(W_steps + i)
+        ev[i][0].record(stream)
+        c["step"]()
+        ev[i][1].record(stream)
+    enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {K_steps} sparse steps: {wall * 1e3:.2f} ms")
-
-    seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     ms_per_step = wall * 1e3 / K_steps
     qps = w.batch * K_steps / wall
 
-    # per-call algorithmic bytes, averaged over the steps run
     sched = [(W_steps + i) % T for i in range(K_steps)]
     b_upd = np.mean([centroid_bytes(w, len(synth.completed_pages(lay, s))) for s in sched])
     b_idx = np.mean([sum(indexer_bytes(w, L) for L in L_steps[s]) for s in sched])
     b_dec = np.mean([sum(attention_bytes(w, L) for L in L_steps[s]) for s in sched])
-    units = {
-        "centroid_update": (b_upd, float(seg[:, 0].mean())),
-        "score_topk": (b_idx, float(seg[:, 1].mean())),
-        "sparse_paged_decode": (b_dec, float(seg[:, 2].mean())),
+    b_step = b_upd + b_idx + b_dec
+    call_ms = float(step_ms.mean())
+    achieved = b_step / (call_ms * 1e-3) / 1e9
+    step_gbps = b_step / (ms_per_step * 1e-3) / 1e9
+
+    # ---------------- the same work as separate calls (per-stage breakdown)
+    n_sep = max(K_steps // 2, 1)
+    for i in range(min(W_steps, 8)):
+        c = schedule(i)
+        if c["upd"]:
+            c["upd"]()
+        c["idx"]()
+        c["dec"]()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_sep)]
+    t1 = time.perf_counter()
+    for i in range(n_sep):
+        c = schedule(W_steps + i)
+        e = evs[i]
+        e[0].record(stream)
+        if c["upd"]:
+            c["upd"]()
+        e[1].record(stream)
+        c["idx"]()
+        e[2].record(stream)
+        c["dec"]()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    sep_wall = time.perf_counter() - t1
+    seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    separate = {
+        "ms_per_step": sep_wall * 1e3 / n_sep,
+        "queries_per_s": w.batch * n_sep / sep_wall,
+        "calls": {k: {"bytes_per_call": int(bb), "avg_ms": float(seg[:, j].mean()),
+                      "gbps": bb / (seg[:, j].mean() * 1e-3) / 1e9 if seg[:, j].mean() > 0 else None}
+                  for j, (k, bb) in enumerate((("vx_centroid_update", b_upd),
+                                                ("vx_score_topk", b_idx),
+                                                ("vx_sparse_paged_decode", b_dec)))},
     }
-    kernels = {k: {"bytes_per_call": int(bb), "avg_ms": ms,
-                   "gbps": (bb / (ms * 1e-3) / 1e9) if ms > 0 else None}
-               for k, (bb, ms) in units.items()}
-    dom = max(units, key=lambda k: units[k][1])
-    bb, ms = units[dom]
-    achieved = bb / (ms * 1e-3) / 1e9
-    step_gbps = (b_upd + b_idx + b_dec) / (ms_per_step * 1e-3) / 1e9
+    log(f"separate calls: {separate['ms_per_step']:.4f} ms/step")
 
     # ---------------- dense comparator
     dense = None
     if not args.no_dense:
         nd = args.dense_steps
         for i in range(min(4, nd)):
-            schedule(i)[3]()
+            schedule(i)["full"]()
         torch.cuda.synchronize()
         evd = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nd)]
         t1 = time.perf_counter()
         for i in range(nd):
             evd[i][0].record(stream)
-            schedule(W_steps + i)[3]()
+            schedule(W_steps + i)["full"]()
             evd[i][1].record(stream)
         torch.cuda.synchronize()
         dwall = time.perf_counter() - t1
@@ -317,13 +351,14 @@ def main():
         "achieved_gbps": step_gbps,
         "pct_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "speedup_vs_dense": (dense["ms_per_step"] / ms_per_step) if dense else None,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "vx_sparse_decode_step",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
         "cpu_baseline": cpu,
-        "step_ms_p10_p50_p90": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
-        "algorithmic_bytes_per_step": int(b_upd + b_idx + b_dec),
-        "kernels": kernels,
+        "algorithmic_bytes_per_step": int(b_step),
+        "step_call_ms_p10_p50_p90": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
+        "host_enqueue_us_per_step": enqueue * 1e6 / K_steps,
+        "separate_calls": separate,
         "dense": dense,
     }
     print(json.dumps(line), flush=True)

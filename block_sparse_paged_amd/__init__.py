@@ -28,12 +28,12 @@ VX_ERR_WORKSPACE_TOO_SMALL = 3
 VX_ERR_HIP = 4
 
 VX_F32, VX_BF16 = 0, 1
-VX_OP_SCORE_TOPK, VX_OP_SPARSE_DECODE, VX_OP_FULL_DECODE = 0, 1, 2
+VX_OP_SCORE_TOPK, VX_OP_SPARSE_DECODE, VX_OP_FULL_DECODE, VX_OP_DECODE_STEP = 0, 1, 2, 3
 
 # Symbols include/vx.h declares (checked by the ABI tests).
 EXPORTS = ("vx_centroid_update", "vx_score_topk", "vx_sparse_paged_decode",
-           "vx_full_paged_decode", "vx_workspace_size", "vx_set_pages_per_split",
-           "vx_status_string", "vx_version")
+           "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
+           "vx_set_pages_per_split", "vx_status_string", "vx_version")
 
 
 class VxError(RuntimeError):
@@ -80,14 +80,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_score_topk.argtypes = [kvp, btp, VP, I32, I32, I32, VP, VP, SZ, VP]
     lib.vx_sparse_paged_decode.argtypes = [kvp, btp, VP, VP, I32, F32, VP, VP, VP, SZ, VP]
     lib.vx_full_paged_decode.argtypes = [kvp, btp, VP, F32, VP, VP, VP, SZ, VP]
+    lib.vx_sparse_decode_step.argtypes = [kvp, btp, VP, I32, I32, I32, I32, F32, VP, VP, VP,
+                                          VP, SZ, VP]
     lib.vx_workspace_size.argtypes = [I32, kvp, btp, I32, P(SZ)]
     lib.vx_set_pages_per_split.argtypes = [I32]
     lib.vx_status_string.argtypes = [I32]
     lib.vx_status_string.restype = ctypes.c_char_p
     lib.vx_version.argtypes = []
     for name in ("vx_centroid_update", "vx_score_topk", "vx_sparse_paged_decode",
-                 "vx_full_paged_decode", "vx_workspace_size", "vx_set_pages_per_split",
-                 "vx_version"):
+                 "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
+                 "vx_set_pages_per_split", "vx_version"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -218,6 +220,15 @@ def full_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sm_scale: floa
         _ptr(workspace), workspace.numel(), _stream(stream)), "vx_full_paged_decode")
 
 
+def sparse_decode_step(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
+                       n_eos: int, update_completed: bool, sm_scale: float, sel: torch.Tensor,
+                       out: torch.Tensor, lse: Optional[torch.Tensor], workspace: torch.Tensor,
+                       stream=None):
+    """vx_sparse_decode_step: completed-page centroids, selection and attention."""
+    prepare_sparse_decode_step(kv, batch, q, topk, n_bos, n_eos, update_completed, sm_scale,
+                               sel, out, lse, workspace, stream)()
+
+
 def set_pages_per_split(n: int):
     """Test hook: force the decode split size (0 = planner)."""
     _check(load_library().vx_set_pages_per_split(int(n)), "vx_set_pages_per_split")
@@ -287,3 +298,18 @@ def prepare_full_paged_decode(kv: PagedKV, batch: Batch, q, sm_scale, out, lse, 
             _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
     return PreparedCall(lib.vx_full_paged_decode, args, "vx_full_paged_decode",
                         (kvs, bs, kv, batch, q, out, lse, workspace))
+
+
+def prepare_sparse_decode_step(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos,
+                               update_completed, sm_scale, sel, out, lse, workspace,
+                               stream=None) -> PreparedCall:
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    _need(out, "out")
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos,
+            1 if update_completed else 0, float(sm_scale), _ptr(sel), _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall(lib.vx_sparse_decode_step, args, "vx_sparse_decode_step",
+                        (kvs, bs, kv, batch, q, sel, out, lse, workspace))

@@ -35,6 +35,22 @@ constexpr size_t kAlign = 256;
 
 int g_pages_per_split_override = 0;
 
+// Largest LDS allocation one block may use on the current device (cached
+// per device; 64 KiB if the query fails).
+size_t max_lds_per_block() {
+  static size_t cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+  if (!cached[dev]) {
+    int v = 0;
+    cached[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+                       hipSuccess && v > 0)
+                      ? (size_t)v
+                      : 65536;
+  }
+  return cached[dev];
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 int elem_bytes(int dtype) { return dtype == VX_F32 ? 4 : 2; }
@@ -190,31 +206,9 @@ vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
   return hip_status(e);
 }
 
-}  // namespace
-
-extern "C" {
-
-vx_status vx_centroid_update(const vx_paged_kv* kv, const int32_t* page_ids, int32_t n_ids,
-                             hipStream_t stream) {
-  vx_status st = check_kv(kv);
-  if (st != VX_OK) return st;
-  if (n_ids < 0) return VX_ERR_INVALID_ARGUMENT;
-  if (n_ids == 0) return VX_OK;
-  if (!page_ids || !kv->k_cache || !kv->centroids) return VX_ERR_INVALID_ARGUMENT;
-  CentroidArgs a{};
-  a.k = kv->k_cache;
-  a.cent = kv->centroids;
-  a.ids = page_ids;
-  a.n_ids = n_ids;
-  a.H_kv = kv->num_kv_heads;
-  a.S_p = kv->page_size;
-  a.D = kv->head_dim_qk;
-  return hip_status(launch_centroid(kv->dtype, a, stream));
-}
-
-vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
-                        int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                          int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   vx_status st = check_kv(kv);
   if (st != VX_OK) return st;
   if ((st = check_batch(kv, batch)) != VX_OK) return st;
@@ -270,6 +264,7 @@ vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void
     s.max_tokens = max_tokens;
     s.n_bos = n_bos;
     s.n_eos = n_eos;
+    s.scores = scores;     // not read by the fused kernel
     return hip_status(launch_indexer_fused(kv->dtype, s, t, stream));
   }
 
@@ -295,11 +290,58 @@ vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void
     const long long total = (long long)batch->batch * max_cand;
     int cpb = ceil_div(total, 2048);
     cpb = std::min(std::max(cpb, 32), 256);
+    // the group-mean query each block forms reads H_q*D elements: keep it
+    // well below the block's centroid bytes (cpb*H_kv*D)
+    const int G = batch->num_q_heads / kv->num_kv_heads;
+    cpb = std::max(cpb, std::min(4 * G, 256));
     s.cand_per_block = cpb;
     hipError_t e = launch_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
     if (e != hipSuccess) return VX_ERR_HIP;
   }
   return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
+}
+
+size_t step_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
+  return std::max(score_ws_bytes(kv, bt), plan_decode(kv, bt, k_tot, true).ws_bytes());
+}
+
+// Dynamic LDS of the fused step kernel: staged page row and keys (one word
+// per page each) and the selected list; plus its static arrays.
+size_t step_lds_bytes(int max_pages, int k_tot, int D, int G) {
+  const size_t dyn = (2 * (size_t)max_pages + (size_t)k_tot) * 4;
+  const size_t stat = (size_t)D * 4 + 4 * 256 * 4 + 2 * 8 * 4 * 3 + 8 * (size_t)G * (D + 2) * 4;
+  return dyn + stat;
+}
+
+}  // namespace
+
+extern "C" {
+
+vx_status vx_centroid_update(const vx_paged_kv* kv, const int32_t* page_ids, int32_t n_ids,
+                             hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if (n_ids < 0) return VX_ERR_INVALID_ARGUMENT;
+  if (n_ids == 0) return VX_OK;
+  if (!page_ids || !kv->k_cache || !kv->centroids) return VX_ERR_INVALID_ARGUMENT;
+  CentroidArgs a{};
+  a.k = kv->k_cache;
+  a.cent = kv->centroids;
+  a.ids = page_ids;
+  a.pt = nullptr;
+  a.seq_lens = nullptr;
+  a.n_ids = n_ids;
+  a.H_kv = kv->num_kv_heads;
+  a.S_p = kv->page_size;
+  a.D = kv->head_dim_qk;
+  return hip_status(launch_centroid(kv->dtype, a, stream));
+}
+
+vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                        int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return score_topk_impl(kv, batch, q, topk, n_bos, n_eos, sel, workspace, workspace_bytes,
+                         stream);
 }
 
 vx_status vx_sparse_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
@@ -334,6 +376,104 @@ vx_status vx_full_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, con
                     stream);
 }
 
+vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                                int32_t topk, int32_t n_bos, int32_t n_eos,
+                                int32_t update_completed, float sm_scale, int32_t* sel,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (topk < 0 || n_bos < 0 || n_eos < 1) return VX_ERR_INVALID_ARGUMENT;
+  if ((long long)topk + n_bos + n_eos > 0x7fffffffLL) return VX_ERR_INVALID_ARGUMENT;
+  if (update_completed != 0 && update_completed != 1) return VX_ERR_INVALID_ARGUMENT;
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !sel || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) ||
+      !kv->centroids || !batch->page_table || !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  const int mp = max_pages_eff(kv, batch);
+  if (mp > kMaxCandidates) return VX_ERR_UNSUPPORTED;
+  const int k_tot = topk + n_bos + n_eos;
+  if (workspace_bytes < step_ws_bytes(kv, batch, k_tot)) return VX_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return VX_ERR_INVALID_ARGUMENT;
+  const int G = batch->num_q_heads / kv->num_kv_heads;
+  const long long units = (long long)batch->batch * kv->num_kv_heads;
+
+  // One block per (request, KV head) runs the whole step when there are
+  // enough of them to fill the GPU (or the problem is tiny) and its LDS fits.
+  if (!is_mla(kv) && decode_step_supported(kv->dtype, kv->head_dim_qk, G) &&
+      (units >= kNumCUs / 2 || units * mp <= 4096) &&
+      step_lds_bytes(mp, k_tot, kv->head_dim_qk, G) <= max_lds_per_block()) {
+    StepArgs a{};
+    DecodeArgs& d = a.d;
+    d.q = q;
+    d.k = kv->k_cache;
+    d.v = kv->v_aliases_k ? kv->k_cache : kv->v_cache;
+    d.pt = batch->page_table;
+    d.seq_lens = batch->seq_lens;
+    d.B = batch->batch;
+    d.H_q = batch->num_q_heads;
+    d.H_kv = kv->num_kv_heads;
+    d.S_p = kv->page_size;
+    d.pt_stride = batch->max_pages_per_req;
+    d.k_tot = k_tot;
+    d.max_tokens = batch->max_seq_len;
+    d.pages_per_split = k_tot;
+    d.n_split = 1;
+    d.v_stride_tok = kv->v_aliases_k ? kv->head_dim_qk : kv->head_dim_v;
+    d.scale_log2 = sm_scale * 1.4426950408889634f;
+    d.out = out;
+    d.lse = lse;
+    ScoreArgs& sc = a.s;
+    sc.q = q;
+    sc.cent = kv->centroids;
+    sc.pt = batch->page_table;
+    sc.seq_lens = batch->seq_lens;
+    sc.scores = reinterpret_cast<float*>(workspace);   // not read by the fused kernel
+    sc.B = batch->batch;
+    sc.H_q = batch->num_q_heads;
+    sc.H_kv = kv->num_kv_heads;
+    sc.D = kv->head_dim_qk;
+    sc.S_p = kv->page_size;
+    sc.pt_stride = batch->max_pages_per_req;
+    sc.score_stride = mp;
+    sc.max_tokens = batch->max_seq_len;
+    sc.n_bos = n_bos;
+    sc.n_eos = n_eos;
+    a.sel = sel;
+    a.cent = kv->centroids;
+    a.topk = topk;
+    a.n_bos = n_bos;
+    a.n_eos = n_eos;
+    a.k_tot = k_tot;
+    a.max_pages = mp;
+    a.update_completed = update_completed;
+    return hip_status(launch_decode_step(kv->dtype, kv->head_dim_qk, G, a, stream));
+  }
+
+  // Otherwise: completed-page centroids, the indexer, then attention.
+  if (update_completed) {
+    CentroidArgs c{};
+    c.k = kv->k_cache;
+    c.cent = kv->centroids;
+    c.ids = nullptr;
+    c.pt = batch->page_table;
+    c.seq_lens = batch->seq_lens;
+    c.n_ids = batch->batch;
+    c.H_kv = kv->num_kv_heads;
+    c.S_p = kv->page_size;
+    c.D = kv->head_dim_qk;
+    c.pt_stride = batch->max_pages_per_req;
+    c.max_tokens = batch->max_seq_len;
+    if (launch_centroid(kv->dtype, c, stream) != hipSuccess) return VX_ERR_HIP;
+  }
+  st = score_topk_impl(kv, batch, q, topk, n_bos, n_eos, sel, workspace, workspace_bytes, stream);
+  if (st != VX_OK) return st;
+  return run_decode(kv, batch, q, sel, k_tot, sm_scale, out, lse, workspace, workspace_bytes,
+                    stream);
+}
+
 vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* batch,
                             int32_t k_tot, size_t* bytes) {
   if (!bytes) return VX_ERR_INVALID_ARGUMENT;
@@ -351,6 +491,11 @@ vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* b
       return VX_OK;
     case VX_OP_FULL_DECODE:
       *bytes = plan_decode(kv, batch, max_pages_eff(kv, batch), false).ws_bytes();
+      return VX_OK;
+    case VX_OP_DECODE_STEP:
+      if (max_pages_eff(kv, batch) > kMaxCandidates) return VX_ERR_UNSUPPORTED;
+      if (k_tot < 1) return VX_ERR_INVALID_ARGUMENT;
+      *bytes = step_ws_bytes(kv, batch, k_tot);
       return VX_OK;
   }
   return VX_ERR_INVALID_ARGUMENT;

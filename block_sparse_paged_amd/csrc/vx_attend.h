@@ -1,0 +1,221 @@
+// Exact softmax attention of one (request, KV head)'s query group over a list
+// of logical pages, computed by one block of 8 waves (VALU path, D_qk = D_v =
+// D).  Shared by the split-K decode kernel and the fused decode step.
+//
+// Lanes hold 16-byte segments of a token row: L = D*e/16 lanes per row,
+// R = 64/L rows (tokens) per wave-load, so one wave-load reads 1 KiB of a
+// page-head tile contiguously.  Each lane group of L lanes runs its own online
+// softmax over the tokens it holds (per-token dot products reduced with DPP
+// row moves), so nothing crosses lane groups inside the loop.  Waves take the
+// list's pages round-robin with PF 16-token chunks of K and V in flight; with
+// G = 8 the two halves of the query group go to different waves over the same
+// pages (register pressure).  Lane groups merge with shuffles, waves through
+// LDS; the block then writes the normalised output and lse, or fp32 partials
+// (unnormalised sum, max in log2 units, denominator) for a later merge.
+#pragma once
+
+#include "vx_device.h"
+#include "vx_internal.h"
+
+namespace vx {
+
+constexpr int kChunk = 16;   // tokens per softmax update
+constexpr int kNW = 8;       // waves per attention block
+
+// page_at(idx) returns {logical page, physical page} of list entry idx; it is
+// called by every lane (inactive lanes pass active = false and get ignored).
+template <typename T, int D, int G, int HS, int PF, class PageAt>
+__device__ __forceinline__ void attend_pages(const DecodeArgs& a, int b, int h, int split,
+                                             int p0, int p1, int seq, PageAt page_at) {
+  using V = Vec16<T>;
+  constexpr int E = V::E;
+  constexpr int L = D / E;          // lanes per token row
+  constexpr int R = 64 / L;         // token rows per wave-load
+  constexpr int NL = kChunk / R;    // wave-loads per chunk (K and V each)
+  constexpr int HG = G / HS;        // query heads per wave
+  constexpr int NWP = kNW / HS;     // waves working on different pages
+  static_assert(L * R == 64 && NL * R == kChunk && HG * HS == G, "layout");
+
+  __shared__ float s_m[kNW][HG], s_l[kNW][HG];
+  __shared__ float s_o[kNW][HG][D];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int seg = lane % L, grp = lane / L;
+  const int hs = w % HS, wp = w / HS;
+  const int SP = a.S_p;
+  const int hq0 = h * G + hs * HG;
+
+  float q[HG][E];
+  {
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.H_q + hq0) * D + seg * E;
+#pragma unroll
+    for (int g = 0; g < HG; ++g) {
+      V::unpack(ld16(qp + (size_t)g * D), q[g]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) q[g][e] *= a.scale_log2;
+    }
+  }
+
+  float o[HG][E], l[HG], m[HG];
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    l[g] = 0.f;
+    m[g] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[g][e] = 0.f;
+  }
+
+  const T* kbase = reinterpret_cast<const T*>(a.k);
+  const T* vbase = reinterpret_cast<const T*>(a.v);
+  const size_t tile_k = (size_t)SP * D;
+  const size_t vtok = (size_t)a.v_stride_tok;
+  const size_t tile_v = (size_t)SP * vtok;
+  const int cpp = SP / kChunk;
+  const int my_n = p1 > p0 + wp ? (p1 - p0 - wp + NWP - 1) / NWP : 0;
+
+  for (int base = 0; base < my_n; base += 64) {
+    const int nb = min(64, my_n - base);
+    const int idx = p0 + wp + NWP * (base + lane);
+    const int2 lp = page_at(idx, lane < nb);
+    const int logi_l = lane < nb ? lp.x : 0, phys_l = lane < nb ? lp.y : 0;
+    const int nch = nb * cpp;
+    uint4 kb[PF][NL], vb[PF][NL];
+    auto issue = [&](int c, uint4* kd, uint4* vd) {
+      const int j = c / cpp, ch = c - j * cpp;
+      const int phys = __builtin_amdgcn_readlane(phys_l, j);
+      const T* kp = kbase + ((size_t)phys * a.H_kv + h) * tile_k + (size_t)(ch * kChunk) * D;
+      const T* vp = vbase + ((size_t)phys * a.H_kv + h) * tile_v + (size_t)(ch * kChunk) * vtok;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int t = i * R + grp;
+        kd[i] = ld16(kp + (size_t)t * D + seg * E);
+        vd[i] = ld16(vp + (size_t)t * vtok + seg * E);
+      }
+    };
+    auto process = [&](int c, const uint4* kd, const uint4* vd) {
+      const int j = c / cpp, ch = c - j * cpp;
+      const int logi = __builtin_amdgcn_readlane(logi_l, j);
+      const int tok0 = logi * SP + ch * kChunk;
+      float s[HG][NL];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        float kf[E];
+        V::unpack(kd[i], kf);
+        const bool valid = tok0 + i * R + grp < seq;
+#pragma unroll
+        for (int g = 0; g < HG; ++g) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc = fmaf(q[g][e], kf[e], acc);
+          acc = lane_group_sum<L>(acc);
+          s[g][i] = valid ? acc : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < HG; ++g) {
+        float mc = s[g][0];
+#pragma unroll
+        for (int i = 1; i < NL; ++i) mc = fmaxf(mc, s[g][i]);
+        const float mn = fmaxf(m[g], mc);
+        const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[g] - mn);
+        m[g] = mn;
+        l[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[g][e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const float p = (mn == -INFINITY) ? 0.f : exp2f(s[g][i] - mn);
+          s[g][i] = p;
+          l[g] += p;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        float vf[E];
+        V::unpack(vd[i], vf);
+#pragma unroll
+        for (int g = 0; g < HG; ++g)
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[g][e] = fmaf(s[g][i], vf[e], o[g][e]);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (u < nch) issue(u, kb[u], vb[u]);
+    for (int c0 = 0; c0 < nch; c0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int c = c0 + u;
+        if (c < nch) {
+          process(c, kb[u], vb[u]);
+          if (c + PF < nch) issue(c + PF, kb[u], vb[u]);
+        }
+      }
+    }
+  }
+
+  // merge the lane groups of this wave, then the waves of the block
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    const float mw = across_groups_max<L>(m[g]);
+    const float sc = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - mw);
+    const float lw = across_groups_sum<L>(l[g] * sc);
+    float ow[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ow[e] = across_groups_sum<L>(o[g][e] * sc);
+    if (grp == 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_o[w][g][seg * E + e] = ow[e];
+      if (seg == 0) {
+        s_m[w][g] = mw;
+        s_l[w][g] = lw;
+      }
+    }
+  }
+  __syncthreads();
+
+  const bool direct = a.n_split == 1;
+  for (int i = tid; i < G * D; i += kNW * 64) {
+    const int gg = i / D, d = i - gg * D;
+    const int hs2 = gg / HG, g = gg - hs2 * HG;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NWP; ++v) M = fmaxf(M, s_m[v * HS + hs2][g]);
+    float Ls = 0.f, Os = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWP; ++v) {
+      const int ww = v * HS + hs2;
+      const float wt = (s_m[ww][g] == -INFINITY) ? 0.f : exp2f(s_m[ww][g] - M);
+      Ls += wt * s_l[ww][g];
+      Os += wt * s_o[ww][g][d];
+    }
+    const size_t row = (size_t)b * a.H_q + h * G + gg;
+    if (direct) {
+      T* op = reinterpret_cast<T*>(a.out) + row * D;
+      op[d] = V::from_f32(Ls > 0.f ? Os / Ls : 0.f);
+      if (d == 0 && a.lse) a.lse[row] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+    } else {
+      const size_t prow = row * a.n_split + split;
+      a.part_o[prow * D + d] = Os;
+      if (d == 0) {
+        a.part_ml[prow * 2] = M;
+        a.part_ml[prow * 2 + 1] = Ls;
+      }
+    }
+  }
+}
+
+// Chunks of K and V kept in flight per wave: two, or one where 32 lanes per
+// row (fp32, D = 128) make a chunk of K and V 64 registers.
+template <typename T, int D>
+constexpr int attend_prefetch() {
+  return (sizeof(T) == 4 && D == 128) ? 1 : 2;
+}
+
+// Query-head slices per wave group: the G = 8 group is split in two halves.
+template <int G>
+constexpr int attend_head_slices() {
+  return G == 8 ? 2 : 1;
+}
+
+}  // namespace vx

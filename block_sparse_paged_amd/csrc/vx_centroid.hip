@@ -9,21 +9,13 @@
 // t / SEGS + RG, ..., all issued before the first is used, keeping fp32 sums;
 // the RG row groups are then added in a fixed order through LDS, scaled by
 // 1/S_p (exact: S_p is a power of two) and rounded once.
-#include "vx_device.h"
+#include "vx_centroid.h"
 #include "vx_internal.h"
 
 namespace vx {
 namespace {
 
 constexpr int kMaxRowsPerThread = 8;
-
-template <typename T, int D>
-struct CentroidShape {
-  static constexpr int E = Vec16<T>::E;
-  static constexpr int SEGS = D / E;                       // 16-byte segments per row
-  static constexpr int RG = (SEGS * 16 <= 1024) ? 16 : 1024 / SEGS;   // row groups
-  static constexpr int THREADS = SEGS * RG;
-};
 
 template <typename T, int D, int NT>
 __global__ __launch_bounds__(NT) void centroid_kernel(CentroidArgs a) {
@@ -33,7 +25,18 @@ __global__ __launch_bounds__(NT) void centroid_kernel(CentroidArgs a) {
   __shared__ float red[RG][SEGS * E];
   const int tid = threadIdx.x;
   const int seg = tid % SEGS, rg = tid / SEGS;
-  const int page = a.ids[blockIdx.x], h = blockIdx.y;
+  int page;
+  if (a.ids) {
+    page = a.ids[blockIdx.x];
+  } else {
+    // the page that request blockIdx.x's latest token completed, if any
+    const int b = blockIdx.x;
+    int seq = a.seq_lens[b];
+    seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
+    if (seq == 0 || seq % a.S_p != 0) return;
+    page = a.pt[(size_t)b * a.pt_stride + seq / a.S_p - 1];
+  }
+  const int h = blockIdx.y;
   const T* kp = reinterpret_cast<const T*>(a.k) + ((size_t)page * a.H_kv + h) * (size_t)a.S_p * D;
 
   uint4 buf[kMaxRowsPerThread];
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(NT) void centroid_kernel(CentroidArgs a) {
   for (int e = 0; e < E; ++e) red[rg][seg * E + e] = acc[e];
   __syncthreads();
   if (tid < SEGS) {
+    // same order as centroid_segment(): groups in order, then the scale
     const float inv = 1.0f / (float)a.S_p;
     float sum[E];
 #pragma unroll

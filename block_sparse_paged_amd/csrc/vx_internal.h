@@ -14,8 +14,12 @@ namespace vx {
 struct CentroidArgs {
   const void* k;          // [P, H_kv, S_p, D]
   void* cent;             // [P, H_kv, D]
-  const int32_t* ids;     // [n_ids]
+  const int32_t* ids;     // [n_ids] physical pages, or nullptr: one block row per request,
+                          // updating the page its latest token completed (if any)
+  const int32_t* pt;      // [B, pt_stride] (ids == nullptr)
+  const int32_t* seq_lens;
   int32_t n_ids, H_kv, S_p, D;
+  int32_t pt_stride, max_tokens;
 };
 
 struct ScoreArgs {
@@ -54,6 +58,18 @@ struct DecodeArgs {
   float scale_log2;       // sm_scale * log2(e)
 };
 
+// One fused decode step per (request, KV head) block: completed-page
+// centroid, indexer and attention over the selection.
+struct StepArgs {
+  DecodeArgs d;           // attention (n_split = 1; sel unused)
+  ScoreArgs s;            // indexer (scores unused)
+  int32_t* sel;           // [B, H_kv, k_tot]
+  void* cent;             // centroid table, written for completed pages
+  int32_t topk, n_bos, n_eos, k_tot;
+  int32_t max_pages;      // page-table entries staged in LDS per request
+  int32_t update_completed;
+};
+
 struct CombineArgs {
   const float* part_o;
   const float* part_ml;
@@ -73,5 +89,7 @@ hipError_t launch_decode_valu(int dtype, int D, int G, const DecodeArgs& a, hipS
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 int mla_max_pages_per_split();
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
+bool decode_step_supported(int dtype, int D, int G);
+hipError_t launch_decode_step(int dtype, int D, int G, const StepArgs& a, hipStream_t s);
 
 }  // namespace vx

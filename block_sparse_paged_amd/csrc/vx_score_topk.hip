@@ -24,8 +24,7 @@
 // an early stop once the boundary bin is taken whole), equal keys ranked by
 // page, then the union with the reserved pages is compacted in ascending
 // page order with one block-wide scan.
-#include "vx_device.h"
-#include "vx_internal.h"
+#include "vx_select.h"
 
 namespace vx {
 namespace {
@@ -35,135 +34,17 @@ constexpr int kTopkThreads = 256;
 constexpr int kFusedThreads = 512;
 constexpr int kLoadsInFlight = 16;   // wave-loads issued before the first is used
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 and +0 are equal
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive scan of one int per thread over an NT-thread block, in thread
-// order.  `tmp` holds NT/64 ints of LDS.  Also returns the block total.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int inc = wave_inclusive_scan(x);
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int t = tmp[w];
-    base += (w < wave) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + inc - x;
-}
-
-// Selects and writes one (request, KV head) row of `sel`.
-//   keys     LDS, n_cand order-preserving keys of candidates n_bos.. (in page order)
-//   hist     LDS, 4*256 ints, zero on entry
-// Keys and the zeroed histograms must be visible to every thread (the caller
-// synchronises first).
-template <int NT>
-__device__ void select_pages(const uint32_t* keys, int n_cand, int n_b, int topk, int n_bos,
-                             int n_eos, int k_tot, int32_t* out, int* hist, int* scan_tmp) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const bool all = n_cand <= topk;
-  const bool none = !all && topk == 0;
-  uint32_t thr = 0, msk = 0;
-  int take_eq = 0, cnt_eq = 0;
-  if (!all && !none) {
-    int remaining = topk;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      int* H = hist + 256 * pass;
-      for (int i = tid; i < n_cand; i += NT) {
-        const uint32_t k = keys[i];
-        if ((k & msk) == thr) atomicAdd(&H[(k >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      // every wave finds the bin where the count from the top crosses `remaining`
-      const int h0 = H[4 * lane], h1 = H[4 * lane + 1], h2 = H[4 * lane + 2], h3 = H[4 * lane + 3];
-      const int own = h0 + h1 + h2 + h3;
-      int suf = own;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_down(suf, d, 64);
-        if (lane + d < 64) suf += y;
-      }
-      int acc = suf - own, dsel = -1, above = 0, cnt = 0;
-      if (acc < remaining && acc + h3 >= remaining) { dsel = 4 * lane + 3; above = acc; cnt = h3; }
-      acc += h3;
-      if (dsel < 0 && acc < remaining && acc + h2 >= remaining) { dsel = 4 * lane + 2; above = acc; cnt = h2; }
-      acc += h2;
-      if (dsel < 0 && acc < remaining && acc + h1 >= remaining) { dsel = 4 * lane + 1; above = acc; cnt = h1; }
-      acc += h1;
-      if (dsel < 0 && acc < remaining && acc + h0 >= remaining) { dsel = 4 * lane; above = acc; cnt = h0; }
-      const unsigned long long found = __ballot(dsel >= 0);
-      const int src = __builtin_ctzll(found);
-      const int d = __builtin_amdgcn_readlane(dsel, src);
-      above = __builtin_amdgcn_readlane(above, src);
-      cnt = __builtin_amdgcn_readlane(cnt, src);
-      remaining -= above;
-      thr |= (uint32_t)d << shift;
-      msk |= 0xFFu << shift;
-      cnt_eq = cnt;
-      if (remaining == cnt) break;    // the whole boundary bin is taken
-    }
-    take_eq = remaining;
-  }
-  const bool need_rank = !all && !none && take_eq < cnt_eq;
-
-  // thread tid owns logical pages [p_lo, p_hi)
-  const int per = (n_b + NT - 1) / NT;
-  const int p_lo = min(tid * per, n_b), p_hi = min(p_lo + per, n_b);
-  const int eos_lo = n_b - n_eos;
-  int eq_rank = 0, dummy;
-  if (need_rank) {
-    int n_eq = 0;
-    for (int p = max(p_lo, n_bos); p < min(p_hi, eos_lo); ++p) n_eq += (keys[p - n_bos] & msk) == thr;
-    eq_rank = block_exclusive_scan<NT>(n_eq, scan_tmp, &dummy);
-  }
-  auto take = [&](int p, int& rank) -> bool {
-    if (p < n_bos || p >= eos_lo) return true;
-    if (all || none) return all;
-    const uint32_t km = keys[p - n_bos] & msk;
-    bool t = km > thr;
-    if (km == thr) {
-      t = !need_rank || rank < take_eq;
-      ++rank;
-    }
-    return t;
-  };
-  int r = eq_rank, n_take = 0;
-  for (int p = p_lo; p < p_hi; ++p) n_take += take(p, r) ? 1 : 0;
-  int total;
-  int pos = block_exclusive_scan<NT>(n_take, scan_tmp, &total);
-  r = eq_rank;
-  for (int p = p_lo; p < p_hi; ++p)
-    if (take(p, r)) out[pos++] = p;
-  for (int i = total + tid; i < k_tot; i += NT) out[i] = -1;
-}
-
 // ---------------------------------------------------------------- fused
 template <typename T, int D>
 __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs a, TopkArgs t) {
-  using V = Vec16<T>;
-  constexpr int E = V::E;
-  constexpr int LH = D / E;                  // lanes per centroid row
-  constexpr int R = 64 / LH;                 // rows per wave-load
-  constexpr int NW = kFusedThreads / 64;
-  constexpr int U = kLoadsInFlight;
-  static_assert(LH * R == 64, "fused indexer needs rows of at most 64 lanes");
   extern __shared__ uint32_t dyn[];          // phys [max_cand] then keys [max_cand]
   __shared__ float qbar[D];
   __shared__ int hist[4 * 256];
-  __shared__ int scan_tmp[NW];
+  __shared__ int scan_tmp[kFusedThreads / 64];
+  __shared__ uint32_t bounds_tmp[2 * kFusedThreads / 64];
 
   const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int seg = lane % LH, grp = lane / LH;
+  const int tid = threadIdx.x;
   int seq = a.seq_lens[b];
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
@@ -173,49 +54,19 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs 
   uint32_t* keys = dyn + a.score_stride;
 
   if (scoring) {
-    const int G = a.H_q / a.H_kv;
-    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.H_q + (size_t)h * G) * D;
-    for (int d = tid; d < D; d += kFusedThreads) {
-      float s = 0.f;
-      for (int g = 0; g < G; ++g) s += V::to_f32(qb[(size_t)g * D + d]);
-      qbar[d] = s * (1.0f / (float)G);
-    }
+    head_query_mean<T, D, kFusedThreads>(a, b, h, qbar);
     const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
     for (int i = tid; i < n_cand; i += kFusedThreads) phys[i] = ptb[i];
   }
   for (int i = tid; i < 4 * 256; i += kFusedThreads) hist[i] = 0;
   __syncthreads();
 
-  if (scoring) {
-    float qr[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) qr[e] = qbar[seg * E + e];
-    const T* cent = reinterpret_cast<const T*>(a.cent);
-    constexpr int STEP = NW * R;               // rows per block-wide wave-load
-    for (int r0 = w * R; r0 < n_cand; r0 += STEP * U) {
-      uint4 buf[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = r0 + u * STEP + grp;
-        buf[u] = c < n_cand ? ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + seg * E)
-                            : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = r0 + u * STEP + grp;
-        float f[E];
-        V::unpack(buf[u], f);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc = fmaf(qr[e], f[e], acc);
-        acc = lane_group_sum<LH>(acc);
-        if (seg == 0 && c < n_cand) keys[c] = order_key(acc);
-      }
-    }
-  }
-  __syncthreads();
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  if (scoring) score_head<T, D, kFusedThreads>(a, h, n_cand, phys, qbar, keys, kmax, kmin);
+  block_key_bounds<kFusedThreads>(kmax, kmin, bounds_tmp);
   select_pages<kFusedThreads>(keys, n_cand, n_b, t.topk, t.n_bos, t.n_eos, t.k_tot,
-                              t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, hist, scan_tmp);
+                              t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, nullptr, hist,
+                              scan_tmp, kmax, kmin);
 }
 
 // ---------------------------------------------------------------- split
@@ -297,30 +148,34 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     static_assert(LH > 64 && LH <= 72, "row width");
     constexpr int TL = LH - 64;             // tail segments per row (8)
     constexpr int RT = 64 / TL;             // rows per tile (8)
-    for (int r0 = wave * RT; r0 < rows; r0 += 4 * RT) {
-      uint4 hb[RT], tb;
+    struct Tile { uint4 hb[RT]; uint4 tb; };
+    auto issue = [&](int r0, Tile& tl) {
 #pragma unroll
       for (int i = 0; i < RT; ++i) {
         const int r = r0 + i;
         if (r < rows) {
           const int c = r / a.H_kv, h = r - c * a.H_kv;
-          hb[i] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + lane * E);
+          tl.hb[i] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + lane * E);
         } else {
-          hb[i] = make_uint4(0, 0, 0, 0);
+          tl.hb[i] = make_uint4(0, 0, 0, 0);
         }
       }
       const int tr = r0 + lane / TL, tseg = 64 + lane % TL;
       if (tr < rows) {
         const int c = tr / a.H_kv, h = tr - c * a.H_kv;
-        tb = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + tseg * E);
+        tl.tb = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + tseg * E);
       } else {
-        tb = make_uint4(0, 0, 0, 0);
+        tl.tb = make_uint4(0, 0, 0, 0);
       }
+    };
+    auto consume = [&](int r0, const Tile& tl) {
+      const int tr = r0 + lane / TL, tseg = 64 + lane % TL;
       float tp;
       {
-        const int c = (tr < rows ? tr : 0) / a.H_kv, h = (tr < rows ? tr : 0) - c * a.H_kv;
+        const int trc = tr < rows ? tr : 0;
+        const int c = trc / a.H_kv, h = trc - c * a.H_kv;
         float f[E];
-        V::unpack(tb, f);
+        V::unpack(tl.tb, f);
         const float* qh = qbar + h * D + tseg * E;
         tp = 0.f;
 #pragma unroll
@@ -333,7 +188,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         const int rc = r < rows ? r : 0;
         const int c = rc / a.H_kv, h = rc - c * a.H_kv;
         float f[E];
-        V::unpack(hb[i], f);
+        V::unpack(tl.hb[i], f);
         const float* qh = qbar + h * D + lane * E;
         float acc = 0.f;
 #pragma unroll
@@ -342,6 +197,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tp), i * TL));
         if (lane == 0 && r < rows) out[(size_t)h * a.score_stride + c0 + c] = acc;
       }
+    };
+    // eight rows per tile, two tiles in flight per wave
+    Tile ta, tb;
+    int r0 = wave * RT;
+    if (r0 < rows) issue(r0, ta);
+    for (; r0 < rows; r0 += 8 * RT) {
+      const int r1 = r0 + 4 * RT, r2 = r1 + 4 * RT;
+      if (r1 < rows) issue(r1, tb);
+      consume(r0, ta);
+      if (r2 < rows) issue(r2, ta);
+      if (r1 < rows) consume(r1, tb);
     }
   }
 }
@@ -350,6 +216,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   extern __shared__ uint32_t keys[];        // [n_cand]
   __shared__ int hist[4 * 256];
   __shared__ int scan_tmp[kTopkThreads / 64];
+  __shared__ uint32_t bounds_tmp[2 * kTopkThreads / 64];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;                // b * H_kv + h
@@ -358,14 +225,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
   const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
   if (n_cand > a.topk && a.topk > 0) {
     const float* sc = a.scores + (size_t)bh * a.score_stride;
-    for (int i = tid; i < n_cand; i += kTopkThreads) keys[i] = order_key(sc[i]);
+    for (int i = tid; i < n_cand; i += kTopkThreads) {
+      const uint32_t k = order_key(sc[i]);
+      keys[i] = k;
+      kmax = max(kmax, k);
+      kmin = min(kmin, k);
+    }
   }
   for (int i = tid; i < 4 * 256; i += kTopkThreads) hist[i] = 0;
-  __syncthreads();
+  block_key_bounds<kTopkThreads>(kmax, kmin, bounds_tmp);
   select_pages<kTopkThreads>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
-                             a.sel + (size_t)bh * a.k_tot, hist, scan_tmp);
+                             a.sel + (size_t)bh * a.k_tot, nullptr, hist, scan_tmp, kmax, kmin);
 }
 
 template <typename T, int D>

@@ -78,7 +78,8 @@ typedef enum { VX_F32 = 0, VX_BF16 = 1 } vx_dtype;
 typedef enum {
   VX_OP_SCORE_TOPK = 0,
   VX_OP_SPARSE_DECODE = 1,
-  VX_OP_FULL_DECODE = 2
+  VX_OP_FULL_DECODE = 2,
+  VX_OP_DECODE_STEP = 3
 } vx_op;
 
 /* The paged KV cache and its named centroid cache (the per-page summary
@@ -187,8 +188,32 @@ vx_status vx_full_paged_decode(const vx_paged_kv* kv, const vx_batch* batch,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* One whole decode step, fused (Vortex article, "A dual-stage programmable
+ * abstraction": the cache stage runs when a page is finished, the indexer and
+ * the attention on every step).  Equivalent to, in order:
+ *   - when update_completed == 1, vx_centroid_update on the page each
+ *     request's newest token completed (logical page seq_lens[b]/S_p - 1 of
+ *     requests with seq_lens[b] % S_p == 0);
+ *   - vx_score_topk(kv, batch, q, topk, n_bos, n_eos, sel, ...);
+ *   - vx_sparse_paged_decode(kv, batch, q, sel, topk + n_bos + n_eos,
+ *     sm_scale, out, lse, ...).
+ * The completed page is the last logical page, which is reserved
+ * (n_eos >= 1), so its new centroid cannot change this step's selection.
+ * When there are enough (request, KV head) pairs to fill the GPU, one kernel
+ * does all of it, one block per pair; otherwise the three stages run as
+ * separate launches.  sel and the centroids equal those calls' results bit
+ * for bit; out and lse equal them up to the order of fp32 rounding (bit for
+ * bit when vx_sparse_paged_decode would plan a single split).
+ *   workspace  at least vx_workspace_size(VX_OP_DECODE_STEP, ..., k_tot) bytes
+ * Arguments and errors as for the calls it stands for. */
+vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                                int32_t topk, int32_t n_bos, int32_t n_eos,
+                                int32_t update_completed, float sm_scale, int32_t* sel,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* Workspace bytes the call `op` needs for these shapes (k_tot is read for
- * VX_OP_SPARSE_DECODE only).  Host-only; never touches the GPU.  The size
+ * VX_OP_SPARSE_DECODE and VX_OP_DECODE_STEP only).  Host-only; never touches the GPU.  The size
  * depends on the shapes and on the split override, nothing else. */
 vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* batch,
                             int32_t k_tot, size_t* bytes /* host */);

@@ -223,6 +223,33 @@ def run_full(vx, c: Case, q_dev, ws=None):
     return out, lse
 
 
+def run_step(vx, c: Case, q_dev, update: bool = True, ws=None):
+    """vx_sparse_decode_step: returns (sel, out, lse)."""
+    w = c.w
+    bt = c.batch(vx)
+    sel = torch.empty((w.batch, w.num_kv_heads, w.k_tot), dtype=torch.int32, device=q_dev.device)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype,
+                      device=q_dev.device)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=q_dev.device)
+    if ws is None:
+        ws = vx.alloc_workspace(vx.VX_OP_DECODE_STEP, c.kv, bt, w.k_tot)
+    vx.sparse_decode_step(c.kv, bt, q_dev, w.topk, w.n_bos, w.n_eos, update, w.sm_scale, sel,
+                          out, lse, ws)
+    return sel, out, lse
+
+
+def single_split(vx, c: Case) -> bool:
+    """Whether vx_sparse_paged_decode plans one split for this case."""
+    return vx.workspace_size(vx.VX_OP_SPARSE_DECODE, c.kv, c.batch(vx), c.w.k_tot) == 0
+
+
+def build_setup_centroids(vx, c: Case):
+    """Centroids of the pages full before step 0's token only."""
+    ids = synth.setup_full_pages(c.layout)
+    if len(ids):
+        vx.centroid_update(c.kv, torch.from_numpy(ids.astype(np.int32)).to(c.K.device))
+
+
 def build_centroids(vx, c: Case):
     """Bulk centroids of every page full before step 0, then step 0's completions."""
     ids = np.concatenate([synth.setup_full_pages(c.layout), synth.completed_pages(c.layout, 0)])

@@ -96,6 +96,8 @@ def test_bad_kv_rejected_everywhere(lib, kw, want):
     assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30,
                                     None) == want
     assert ws_size(lib, vx.VX_OP_FULL_DECODE, kv, bt)[0] == want
+    assert lib.vx_sparse_decode_step(r(kv), r(bt), FAKE, 30, 1, 1, 1, 0.1, FAKE, FAKE, FAKE,
+                                     FAKE, 1 << 30, None) == want
 
 
 @pytest.mark.parametrize("kw,want", BAD_BATCH)
@@ -107,7 +109,9 @@ def test_bad_batch_rejected(lib, kw, want):
                                       1 << 30, None) == want
     assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30,
                                     None) == want
-    for op in (0, 1, 2):
+    assert lib.vx_sparse_decode_step(r(kv), r(bt), FAKE, 30, 1, 1, 1, 0.1, FAKE, FAKE, FAKE,
+                                     FAKE, 1 << 30, None) == want
+    for op in (0, 1, 2, 3):
         assert ws_size(lib, op, kv, bt)[0] == want
 
 
@@ -146,6 +150,23 @@ def test_scalar_arguments_rejected(lib):
     for scale in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.vx_full_paged_decode(r(kv), r(bt), FAKE, scale, FAKE, FAKE, FAKE, 1 << 30,
                                         None) == 1
+    step = lib.vx_sparse_decode_step
+    for topk, bos, eos, upd, scale in ((-1, 1, 1, 1, 0.1), (30, -1, 1, 1, 0.1), (30, 1, 0, 1, 0.1),
+                                       (30, 1, 1, 2, 0.1), (30, 1, 1, 1, 0.0),
+                                       (30, 1, 1, 1, float("nan"))):
+        assert step(r(kv), r(bt), FAKE, topk, bos, eos, upd, scale, FAKE, FAKE, FAKE, FAKE,
+                    1 << 30, None) == vx.VX_ERR_INVALID_ARGUMENT
+    for nulls in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
+        assert step(r(kv), r(bt), nulls[0], 30, 1, 1, 1, 0.1, nulls[1], nulls[2], FAKE, FAKE,
+                    1 << 30, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert step(r(kv_struct(centroids=None)), r(bt), FAKE, 30, 1, 1, 1, 0.1, FAKE, FAKE, FAKE,
+                FAKE, 1 << 30, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert step(r(kv), r(batch_struct(batch=0)), None, 30, 1, 1, 1, 0.1, None, None, None, None,
+                0, None) == vx.VX_OK
+    st, need = ws_size(lib, vx.VX_OP_DECODE_STEP, kv, bt, 32)
+    assert st == 0 and need >= ws_size(lib, vx.VX_OP_SCORE_TOPK, kv, bt)[1]
+    assert step(r(kv), r(bt), FAKE, 30, 1, 1, 1, 0.1, FAKE, FAKE, FAKE, FAKE, need - 1,
+                None) == vx.VX_ERR_WORKSPACE_TOO_SMALL
     assert lib.vx_set_pages_per_split(-1) == vx.VX_ERR_INVALID_ARGUMENT
     assert lib.vx_workspace_size(9, r(kv), r(bt), 32, r(ctypes.c_size_t())) == 1
 

@@ -288,3 +288,104 @@ def test_full_size_hetero_sampled(vx):
         H.log(f"  request {b}")
         _check_request(vx, c, b, sel, out, lse)
         _check_request(vx, c, b, None, fo, fl, sparse=False)
+
+
+# ---------------------------------------------------------------- fused step
+@pytest.mark.parametrize("name", SMALL)
+def test_decode_step_equals_separate_calls(vx, name):
+    """vx_sparse_decode_step == centroid update of the completed pages +
+    vx_score_topk + vx_sparse_paged_decode, and matches the oracle."""
+    w = synth.get_workload(name)
+    _mla_guard(vx, w)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    H.fix_gaps(c, range(w.batch))
+    q = c.q_host.cuda()
+    before = c.cent.clone()
+    done = synth.completed_pages(c.layout, 0)
+    if len(done):
+        vx.centroid_update(c.kv, torch.from_numpy(done).cuda())
+    sel1 = H.run_indexer(vx, c, q)
+    out1, lse1 = H.run_sparse(vx, c, q, sel1)
+    after = c.cent.clone()
+    c.cent.copy_(before)
+    sel2, out2, lse2 = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel1, sel2)
+    assert torch.equal(after, c.cent)
+    if H.single_split(vx, c):
+        assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    else:
+        assert (out1.float() - out2.float()).abs().max().item() <= (1e-5 if w.dtype == "f32" else 1e-2)
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel2, out2, lse2)
+    H.assert_centroids(c, np.concatenate([synth.setup_full_pages(c.layout), done]))
+
+
+def test_decode_step_incremental_hetero(vx):
+    """Thirty-two appending steps through vx_sparse_decode_step alone: the
+    centroid table it maintains equals a bulk rebuild bit for bit, and the
+    first and last steps match the oracle."""
+    w = synth.SMALL_WORKLOADS["hetero_small"]
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    for s_ in range(w.steps):
+        H.set_step(c, s_)
+        if s_ in (0, w.steps - 1):
+            H.fix_gaps(c, range(w.batch))
+        q = c.q_host.cuda()
+        sel, out, lse = H.run_step(vx, c, q, update=True)
+        if s_ in (0, w.steps - 1):
+            torch.cuda.synchronize()
+            for b in range(w.batch):
+                _check_request(vx, c, b, sel, out, lse)
+    inc = c.cent.clone()
+    c.cent.zero_()
+    L = synth.step_seq_lens(c.layout, w.steps - 1)
+    ids = np.concatenate([c.layout.page_table[b, :L[b] // w.page_size] for b in range(w.batch)])
+    vx.centroid_update(c.kv, torch.from_numpy(ids.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(ids.astype(np.int64)).cuda()
+    assert torch.equal(inc[idx], c.cent[idx])
+
+
+@pytest.mark.parametrize("topk,bos,eos", [(4, 1, 1), (0, 1, 1), (3, 0, 2)])
+@pytest.mark.parametrize("dtype,D,G,S", [("f32", 64, 1, 16), ("bf16", 128, 8, 16),
+                                         ("bf16", 128, 2, 64)])
+def test_decode_step_edge_lengths(vx, dtype, D, G, S, topk, bos, eos):
+    lens = (1, S - 1, S, S + 1, S * 6, S * 6 + 1, S * 9 + 3)
+    w = synth.Workload(name="edges", batch=len(lens), num_q_heads=2 * G, num_kv_heads=2,
+                       head_dim_qk=D, head_dim_v=D, page_size=S, dtype=dtype, topk=topk,
+                       structure="page_offset", seed=78, seq_lens=lens, n_bos=bos, n_eos=eos,
+                       spare_pages=5)
+    H.log(f"case {H.describe(w)} lens={lens} bos={bos} eos={eos}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    H.fix_gaps(c, range(w.batch))
+    q = c.q_host.cuda()
+    sel, out, lse = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel, out, lse)
+    H.assert_centroids(c, np.concatenate([synth.setup_full_pages(c.layout),
+                                          synth.completed_pages(c.layout, 0)]))
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_b32_l32k", "long_b8_l128k", "mla_b64_l32k"])
+def test_full_size_step_sampled(vx, name):
+    w = synth.get_workload(name)
+    _mla_guard(vx, w)
+    reqs = H.sample_requests(w.batch)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    H.fix_gaps(c, reqs)
+    q = c.q_host.cuda()
+    sel, out, lse = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    for b in reqs:
+        H.log(f"  request {b}")
+        _check_request(vx, c, b, sel, out, lse)
+    H.assert_centroids(c, synth.completed_pages(c.layout, 0))
