@@ -30,7 +30,8 @@ constexpr int kFullTargetBlocks = kNumCUs * 16;
 constexpr int kMlaTargetBlocks = kNumCUs * 2;
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxCandidates = 16384;
-constexpr int kFusedMaxPages = 6144;            // page ids + keys in LDS: 48 KiB
+constexpr int kFusedMaxPages = 6144;
+            // page ids + keys in LDS: 48 KiB
 constexpr size_t kAlign = 256;
 
 int g_pages_per_split_override = 0;
@@ -285,15 +286,11 @@ vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const vo
     s.max_tokens = max_tokens;
     s.n_bos = n_bos;
     s.n_eos = n_eos;
-    // about one block per CU per 4 waves' worth of in-flight loads: 64
-    // candidates (all KV heads) per block, more when the batch is large
-    const long long total = (long long)batch->batch * max_cand;
-    int cpb = ceil_div(total, 2048);
-    cpb = std::min(std::max(cpb, 32), 256);
-    // the group-mean query each block forms reads H_q*D elements: keep it
-    // well below the block's centroid bytes (cpb*H_kv*D)
-    const int G = batch->num_q_heads / kv->num_kv_heads;
-    cpb = std::max(cpb, std::min(4 * G, 256));
+    // about one 8-wave block per CU in all: each request's candidates are
+    // cut into ceil(256 / B) chunks (a multiple of 8 pages, at least 32)
+    const int nblk = std::max(1, ceil_div(kNumCUs, batch->batch));
+    int cpb = ceil_div(max_cand, nblk);
+    cpb = std::max(32, (cpb + 7) / 8 * 8);
     s.cand_per_block = cpb;
     hipError_t e = launch_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
     if (e != hipSuccess) return VX_ERR_HIP;

@@ -29,8 +29,8 @@
 namespace vx {
 namespace {
 
-constexpr int kScoreThreads = 256;
-constexpr int kTopkThreads = 256;
+constexpr int kScoreThreads = 512;
+constexpr int kTopkThreads = 512;
 constexpr int kFusedThreads = 512;
 constexpr int kLoadsInFlight = 16;   // wave-loads issued before the first is used
 
@@ -91,15 +91,24 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int nc = c1 - c0;
   const int tid = threadIdx.x;
 
-  // group-mean query of every KV head, fp32, summed in head order
+  // group-mean query of every KV head, fp32, summed in head order; one
+  // 16-byte segment of one head per thread
   const int G = a.H_q / a.H_kv;
   const T* qb = reinterpret_cast<const T*>(a.q) + (size_t)b * a.H_q * D;
   const float invG = 1.0f / (float)G;
-  for (int i = tid; i < a.H_kv * D; i += kScoreThreads) {
-    const int h = i / D, d = i - h * D;
-    float s = 0.f;
-    for (int g = 0; g < G; ++g) s += V::to_f32(qb[(size_t)(h * G + g) * D + d]);
-    qbar[i] = s * invG;
+  for (int i = tid; i < a.H_kv * LH; i += kScoreThreads) {
+    const int h = i / LH, sg = i - h * LH;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      float f[E];
+      V::unpack(ld16(qb + (size_t)(h * G + g) * D + sg * E), f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) qbar[h * D + sg * E + e] = acc[e] * invG;
   }
   const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
   for (int i = tid; i < nc; i += kScoreThreads) phys[i] = ptb[c0 + i];
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 
   if constexpr (LH <= 64) {
     constexpr int R = 64 / LH;              // rows per wave-load
-    constexpr int STEP = (kScoreThreads / 64) * R;
+    constexpr int STEP = (kScoreThreads / 64) * R;   // rows per block-wide wave-load
     const int seg = lane % LH, grp = lane / LH;
     for (int r0 = wave * R; r0 < rows; r0 += STEP * U) {
       uint4 buf[U];
@@ -199,11 +208,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       }
     };
     // eight rows per tile, two tiles in flight per wave
+    constexpr int NW = kScoreThreads / 64;
     Tile ta, tb;
     int r0 = wave * RT;
     if (r0 < rows) issue(r0, ta);
-    for (; r0 < rows; r0 += 8 * RT) {
-      const int r1 = r0 + 4 * RT, r2 = r1 + 4 * RT;
+    for (; r0 < rows; r0 += 2 * NW * RT) {
+      const int r1 = r0 + NW * RT, r2 = r1 + NW * RT;
       if (r1 < rows) issue(r1, tb);
       consume(r0, ta);
       if (r2 < rows) issue(r2, ta);
