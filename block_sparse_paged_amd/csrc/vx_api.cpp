@@ -122,9 +122,10 @@ DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, boo
     const int n_want = std::max(1, ceil_div(kMlaTargetBlocks, units));
     pps = ceil_div(pages, n_want);
     // partials: G rows of (D_v + 2) fp32, written and read once per split
+    // (the reads mostly hit the on-package cache, hence the loose cap)
     const double kv_bytes = (double)pages * kv->page_size * kv->head_dim_qk * 2;
     while (ceil_div(pages, pps) > 1 &&
-           (double)ceil_div(pages, pps) * G * (kv->head_dim_v + 2) * 8 > 0.25 * kv_bytes)
+           (double)ceil_div(pages, pps) * G * (kv->head_dim_v + 2) * 8 > 0.6 * kv_bytes)
       ++pps;
   } else {
     const int target = sparse ? kSparseTargetBlocks : kFullTargetBlocks;

@@ -56,49 +56,73 @@ __global__ __launch_bounds__(kNW * 64) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // K5: merge the splits of one (request, query head).  Splits with an empty
-// page range have sum 0 and are skipped.
+// page range have sum 0 and are skipped.  256 threads per row; each thread
+// owns D_v/256 output dims (at least one) and keeps eight splits' loads in
+// flight.
+constexpr int kCombineThreads = 256;
+
 template <typename T, int DV>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
-  constexpr int PER = (DV + 63) / 64;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
+  constexpr int PER = (DV + kCombineThreads - 1) / kCombineThreads;
   __shared__ float w[1024];
-  const int lane = threadIdx.x;
+  __shared__ float red[kCombineThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = blockIdx.x;            // b * H_q + hq
   const float* ml = a.part_ml + row * a.n_split * 2;
   float mx = -INFINITY;
-  for (int i = lane; i < a.n_split; i += 64) {
+  for (int i = tid; i < a.n_split; i += kCombineThreads)
     if (ml[2 * i + 1] > 0.f) mx = fmaxf(mx, ml[2 * i]);
-  }
   mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int v = 1; v < kCombineThreads / 64; ++v) mx = fmaxf(mx, red[v]);
+  __syncthreads();
   float tot = 0.f;
-  for (int i = lane; i < a.n_split; i += 64) {
+  for (int i = tid; i < a.n_split; i += kCombineThreads) {
     const float li = ml[2 * i + 1];
     const float wi = li > 0.f ? exp2f(ml[2 * i] - mx) : 0.f;
     w[i] = wi;
     tot += wi * li;
   }
   tot = wave_sum(tot);
+  if (lane == 0) red[wave] = tot;
   __syncthreads();
+  tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < kCombineThreads / 64; ++v) tot += red[v];
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   const float* po = a.part_o + row * a.n_split * DV;
-  for (int i = 0; i < a.n_split; ++i) {
-    const float wi = w[i];
-    if (wi == 0.f) continue;
+  for (int i0 = 0; i0 < a.n_split; i0 += 8) {
+    float x[8][PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int d = j * 64 + lane;
-      if (d < DV) acc[j] = fmaf(wi, po[(size_t)i * DV + d], acc[j]);
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int d = j * kCombineThreads + tid;
+        x[u][j] = (i0 + u < a.n_split && d < DV && w[i0 + u] != 0.f)
+                      ? po[(size_t)(i0 + u) * DV + d] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u < a.n_split) {
+        const float wi = w[i0 + u];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] = fmaf(wi, x[u][j], acc[j]);
+      }
     }
   }
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
   T* op = reinterpret_cast<T*>(a.out) + row * DV;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int d = j * 64 + lane;
+    const int d = j * kCombineThreads + tid;
     if (d < DV) op[d] = Vec16<T>::from_f32(acc[j] * inv);
   }
-  if (lane == 0 && a.lse) a.lse[row] = tot > 0.f ? (mx + __log2f(tot)) * kLn2 : -INFINITY;
+  if (tid == 0 && a.lse) a.lse[row] = tot > 0.f ? (mx + __log2f(tot)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D, int G>
@@ -122,7 +146,7 @@ hipError_t run_decode_g(int G, const DecodeArgs& a, hipStream_t s) {
 
 template <typename T, int DV>
 hipError_t run_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<T, DV>), dim3(a.B * a.H_q), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((combine_kernel<T, DV>), dim3(a.B * a.H_q), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -101,11 +101,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int g = 0; g < G; ++g) {
-      float f[E];
-      V::unpack(ld16(qb + (size_t)(h * G + g) * D + sg * E), f);
+    // eight heads' loads in flight at a time, summed in head order
+    for (int g0 = 0; g0 < G; g0 += 8) {
+      uint4 v[8];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += f[e];
+      for (int j = 0; j < 8; ++j)
+        if (g0 + j < G) v[j] = ld16(qb + (size_t)(h * G + g0 + j) * D + sg * E);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (g0 + j < G) {
+          float f[E];
+          V::unpack(v[j], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] += f[e];
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) qbar[h * D + sg * E + e] = acc[e] * invG;
@@ -123,6 +133,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     constexpr int R = 64 / LH;              // rows per wave-load
     constexpr int STEP = (kScoreThreads / 64) * R;   // rows per block-wide wave-load
     const int seg = lane % LH, grp = lane / LH;
+    // with H_kv dividing STEP every row a lane touches has the same KV head,
+    // so that head's query segment stays in registers
+    const bool fixed_head = STEP % a.H_kv == 0;
+    float qr[E];
+    {
+      const int h0 = (wave * R + grp) % a.H_kv;
+#pragma unroll
+      for (int e = 0; e < E; ++e) qr[e] = qbar[h0 * D + seg * E + e];
+    }
     for (int r0 = wave * R; r0 < rows; r0 += STEP * U) {
       uint4 buf[U];
 #pragma unroll
@@ -142,10 +161,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         const int c = rc / a.H_kv, h = rc - c * a.H_kv;
         float f[E];
         V::unpack(buf[u], f);
-        const float* qh = qbar + h * D + seg * E;
         float acc = 0.f;
+        if (fixed_head) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc = fmaf(qh[e], f[e], acc);
+          for (int e = 0; e < E; ++e) acc = fmaf(qr[e], f[e], acc);
+        } else {
+          const float* qh = qbar + h * D + seg * E;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc = fmaf(qh[e], f[e], acc);
+        }
         acc = lane_group_sum<LH>(acc);
         if (seg == 0 && r < rows) out[(size_t)h * a.score_stride + c0 + c] = acc;
       }

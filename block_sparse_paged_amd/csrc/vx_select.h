@@ -168,12 +168,31 @@ __device__ __forceinline__ void block_key_bounds(uint32_t& kmax, uint32_t& kmin,
 template <typename T, int D, int NT>
 __device__ __forceinline__ void head_query_mean(const ScoreArgs& a, int b, int h, float* qbar) {
   using V = Vec16<T>;
+  constexpr int E = V::E, LH = D / E;
   const int G = a.H_q / a.H_kv;
   const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.H_q + (size_t)h * G) * D;
-  for (int d = threadIdx.x; d < D; d += NT) {
-    float s = 0.f;
-    for (int g = 0; g < G; ++g) s += V::to_f32(qb[(size_t)g * D + d]);
-    qbar[d] = s * (1.0f / (float)G);
+  // one 16-byte segment per thread, eight heads' loads in flight, summed in order
+  for (int sg = threadIdx.x; sg < LH; sg += NT) {
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int g0 = 0; g0 < G; g0 += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (g0 + j < G) v[j] = ld16(qb + (size_t)(g0 + j) * D + sg * E);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (g0 + j < G) {
+          float f[E];
+          V::unpack(v[j], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] += f[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) qbar[sg * E + e] = acc[e] * (1.0f / (float)G);
   }
 }
 
