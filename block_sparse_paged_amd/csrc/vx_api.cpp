@@ -29,6 +29,7 @@ constexpr int kSparseTargetBlocks = kNumCUs;
 constexpr int kFullTargetBlocks = kNumCUs * 16;
 constexpr int kMlaTargetBlocks = kNumCUs * 2;
 constexpr int kMaxSplits = 1024;
+constexpr int kMaxOrderedBatch = 512;
 constexpr int kMaxCandidates = 16384;
 constexpr int kFusedMaxPages = 6144;
             // page ids + keys in LDS: 48 KiB
@@ -305,9 +306,9 @@ size_t step_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
 
 // Dynamic LDS of the fused step kernel: staged page row and keys (one word
 // per page each) and the selected list; plus its static arrays.
-size_t step_lds_bytes(int max_pages, int k_tot, int D, int G) {
-  const size_t dyn = (2 * (size_t)max_pages + (size_t)k_tot) * 4;
-  const size_t stat = (size_t)D * 4 + 4 * 256 * 4 + 2 * 8 * 4 * 3 + 8 * (size_t)G * (D + 2) * 4;
+size_t step_lds_bytes(int max_pages, int k_tot, int D, int G, int ordered_batch) {
+  const size_t dyn = step_dynamic_lds(max_pages, k_tot, ordered_batch);
+  const size_t stat = (size_t)D * 4 + 4 * 256 * 4 + 2 * 8 * 4 * 3 + 8 * (size_t)G * (D + 2) * 4 + 16;
   return dyn + stat;
 }
 
@@ -400,9 +401,14 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
 
   // One block per (request, KV head) runs the whole step when there are
   // enough of them to fill the GPU (or the problem is tiny) and its LDS fits.
+  // With two or more units per CU: 4-wave blocks, two resident per CU, and
+  // (up to 512 requests, where ranking them costs each block little) rows of
+  // blocks taken longest request first.
+  const int waves = units >= 2 * kNumCUs ? 4 : 8;
+  const int ordered = (waves == 4 && batch->batch <= kMaxOrderedBatch) ? batch->batch : 0;
   if (!is_mla(kv) && decode_step_supported(kv->dtype, kv->head_dim_qk, G) &&
       (units >= kNumCUs / 2 || units * mp <= 4096) &&
-      step_lds_bytes(mp, k_tot, kv->head_dim_qk, G) <= max_lds_per_block()) {
+      step_lds_bytes(mp, k_tot, kv->head_dim_qk, G, ordered) <= max_lds_per_block()) {
     StepArgs a{};
     DecodeArgs& d = a.d;
     d.q = q;
@@ -447,7 +453,8 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
     a.k_tot = k_tot;
     a.max_pages = mp;
     a.update_completed = update_completed;
-    return hip_status(launch_decode_step(kv->dtype, kv->head_dim_qk, G, a, stream));
+    a.longest_first = ordered > 0;
+    return hip_status(launch_decode_step(kv->dtype, kv->head_dim_qk, G, waves, a, stream));
   }
 
   // Otherwise: completed-page centroids, the indexer, then attention.

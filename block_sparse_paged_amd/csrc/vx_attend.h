@@ -20,11 +20,12 @@
 namespace vx {
 
 constexpr int kChunk = 16;   // tokens per softmax update
-constexpr int kNW = 8;       // waves per attention block
+constexpr int kNW = 8;       // waves per attention block of the split-K decode
 
 // page_at(idx) returns {logical page, physical page} of list entry idx; it is
 // called by every lane (inactive lanes pass active = false and get ignored).
-template <typename T, int D, int G, int HS, int PF, class PageAt>
+// NW is the block's wave count.
+template <typename T, int D, int G, int HS, int PF, int NW, class PageAt>
 __device__ __forceinline__ void attend_pages(const DecodeArgs& a, int b, int h, int split,
                                              int p0, int p1, int seq, PageAt page_at) {
   using V = Vec16<T>;
@@ -33,11 +34,11 @@ __device__ __forceinline__ void attend_pages(const DecodeArgs& a, int b, int h, 
   constexpr int R = 64 / L;         // token rows per wave-load
   constexpr int NL = kChunk / R;    // wave-loads per chunk (K and V each)
   constexpr int HG = G / HS;        // query heads per wave
-  constexpr int NWP = kNW / HS;     // waves working on different pages
+  constexpr int NWP = NW / HS;      // waves working on different pages
   static_assert(L * R == 64 && NL * R == kChunk && HG * HS == G, "layout");
 
-  __shared__ float s_m[kNW][HG], s_l[kNW][HG];
-  __shared__ float s_o[kNW][HG][D];
+  __shared__ float s_m[NW][HG], s_l[NW][HG];
+  __shared__ float s_o[NW][HG][D];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int seg = lane % L, grp = lane / L;
@@ -175,7 +176,7 @@ __device__ __forceinline__ void attend_pages(const DecodeArgs& a, int b, int h, 
   __syncthreads();
 
   const bool direct = a.n_split == 1;
-  for (int i = tid; i < G * D; i += kNW * 64) {
+  for (int i = tid; i < G * D; i += NW * 64) {
     const int gg = i / D, d = i - gg * D;
     const int hs2 = gg / HG, g = gg - hs2 * HG;
     float M = -INFINITY;

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_valu_kernel(DecodeArgs a) {
     }
     return make_int2(logi, phys);
   };
-  attend_pages<T, D, G, HS, PF>(a, b, h, split, p0, p1, seq, page_at);
+  attend_pages<T, D, G, HS, PF, kNW>(a, b, h, split, p0, p1, seq, page_at);
 }
 
 // K5: merge the splits of one (request, query head).  Splits with an empty

@@ -68,6 +68,7 @@ struct StepArgs {
   int32_t topk, n_bos, n_eos, k_tot;
   int32_t max_pages;      // page-table entries staged in LDS per request
   int32_t update_completed;
+  int32_t longest_first;  // block row r takes the r-th longest request
 };
 
 struct CombineArgs {
@@ -90,6 +91,11 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 int mla_max_pages_per_split();
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
 bool decode_step_supported(int dtype, int D, int G);
-hipError_t launch_decode_step(int dtype, int D, int G, const StepArgs& a, hipStream_t s);
+// Dynamic LDS bytes of a fused step block; ordered_batch = B when block rows
+// go to requests longest first, else 0.
+size_t step_dynamic_lds(int max_pages, int k_tot, int ordered_batch);
+// waves: 4 or 8 per block (one block per (request, KV head)).
+hipError_t launch_decode_step(int dtype, int D, int G, int waves, const StepArgs& a,
+                              hipStream_t s);
 
 }  // namespace vx

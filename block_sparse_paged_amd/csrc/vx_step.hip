@@ -1,5 +1,5 @@
-// Fused decode step of block-top-k sparse attention: one 512-thread block per
-// (request, KV head) runs the whole query-dependent stage and the cache
+// Fused decode step of block-top-k sparse attention: one block per (request,
+// KV head) runs the whole query-dependent stage and the cache
 // update of the page this step's token completed (Vortex article, "A
 // dual-stage programmable abstraction"; vortex_torch README, "Quick Example"):
 //
@@ -15,9 +15,19 @@
 //
 // Steps 2-3 and 4 are the code of vx_score_topk's per-(request, KV head)
 // kernel and of vx_sparse_paged_decode's attention, and step 5 uses the
-// summation order of vx_centroid_update, so the results equal those calls'.
-// One launch replaces four, and the attention phase of each block overlaps
-// the other blocks' scoring instead of waiting for a kernel boundary.
+// summation order of vx_centroid_update, so the selection and the centroids
+// equal those calls' bit for bit; with 8-wave blocks the attention sums in
+// the same order too.  One launch replaces four, and the attention phase of
+// each block overlaps the other blocks' scoring instead of waiting for a
+// kernel boundary.
+//
+// Blocks are 8 waves when there is about one (request, KV head) per CU, so
+// each has the whole CU's memory parallelism; with two or more per CU they
+// are 4 waves, so that two blocks share a CU and one's selection and merge
+// (latency-bound, few loads in flight) overlap the other's streaming.  When
+// the blocks take several rounds of the GPU, rows of blocks go to requests
+// longest first (blocks start in about linear order), so that the long
+// requests of a mixed batch do not start last and run alone at the end.
 #include "vx_attend.h"
 #include "vx_centroid.h"
 #include "vx_select.h"
@@ -25,19 +35,55 @@
 namespace vx {
 namespace {
 
-constexpr int kStepThreads = kNW * 64;
+// Request handled by block row r when rows go to requests in order of
+// decreasing length, ties to the lower index: the request whose rank is r.
+// len: LDS of roundup(B, 4) ints; pick: one LDS int.  Synchronises.
+template <int NT>
+__device__ int longest_first_request(const int32_t* seq_lens, int B, int max_tokens, int r,
+                                     int* len, int* pick) {
+  const int tid = threadIdx.x;
+  const int B4 = (B + 3) & ~3;
+  for (int i = tid; i < B4; i += NT) {
+    int L = -1;   // padding: shorter than any request
+    if (i < B) {
+      L = seq_lens[i];
+      L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
+    }
+    len[i] = L;
+  }
+  __syncthreads();
+  for (int j = tid; j < B; j += NT) {
+    const int Lj = len[j];
+    int rank = 0;
+    for (int i = 0; i < B4; i += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(len + i);
+      rank += (v.x > Lj || (v.x == Lj && i < j)) + (v.y > Lj || (v.y == Lj && i + 1 < j)) +
+              (v.z > Lj || (v.z == Lj && i + 2 < j)) + (v.w > Lj || (v.w == Lj && i + 3 < j));
+    }
+    if (rank == r) *pick = j;
+  }
+  __syncthreads();
+  return *pick;
+}
 
-template <typename T, int D, int G, int HS, int PF>
-__global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
-  extern __shared__ uint32_t dyn[];   // page row [max_pages], keys [max_pages], list [k_tot]
+template <typename T, int D, int G, int HS, int PF, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
+  constexpr int NT = NW * 64;
+  extern __shared__ __align__(16) uint32_t dyn[];   // page row [max_pages], keys [max_pages], list [k_tot]
   __shared__ float qbar[D];
   __shared__ int hist[4 * 256];
-  __shared__ int scan_tmp[kStepThreads / 64];
-  __shared__ uint32_t bounds_tmp[2 * kStepThreads / 64];
+  __shared__ int scan_tmp[NW];
+  __shared__ uint32_t bounds_tmp[2 * NW];
 
-  const int h = blockIdx.x, b = blockIdx.y;
+  __shared__ int pick;
+
+  const int h = blockIdx.x;
   const int tid = threadIdx.x;
   const ScoreArgs& s = a.s;
+  const int b = a.longest_first
+                    ? longest_first_request<NT>(s.seq_lens, s.B, s.max_tokens, blockIdx.y,
+                                                reinterpret_cast<int*>(dyn), &pick)
+                    : blockIdx.y;
   int seq = s.seq_lens[b];
   seq = seq < 0 ? 0 : (seq > s.max_tokens ? s.max_tokens : seq);
   const int SP = s.S_p;
@@ -49,15 +95,15 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
   int32_t* list = reinterpret_cast<int32_t*>(dyn + 2 * a.max_pages);
 
   const int32_t* ptb = s.pt + (size_t)b * s.pt_stride;
-  for (int i = tid; i < n_b; i += kStepThreads) prow[i] = ptb[i];
-  if (scoring) head_query_mean<T, D, kStepThreads>(s, b, h, qbar);
-  for (int i = tid; i < 4 * 256; i += kStepThreads) hist[i] = 0;
+  for (int i = tid; i < n_b; i += NT) prow[i] = ptb[i];
+  if (scoring) head_query_mean<T, D, NT>(s, b, h, qbar);
+  for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0;
   __syncthreads();
 
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  if (scoring) score_head<T, D, kStepThreads>(s, h, n_cand, prow + a.n_bos, qbar, keys, kmax, kmin);
-  block_key_bounds<kStepThreads>(kmax, kmin, bounds_tmp);
-  const int count = select_pages<kStepThreads>(
+  if (scoring) score_head<T, D, NT>(s, h, n_cand, prow + a.n_bos, qbar, keys, kmax, kmin);
+  block_key_bounds<NT>(kmax, kmin, bounds_tmp);
+  const int count = select_pages<NT>(
       keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
       a.sel + ((size_t)b * s.H_kv + h) * a.k_tot, list, hist, scan_tmp, kmax, kmin);
   __syncthreads();
@@ -70,7 +116,7 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
     }
     return make_int2(logi, phys);
   };
-  attend_pages<T, D, G, HS, PF>(a.d, b, h, 0, 0, count, seq, page_at);
+  attend_pages<T, D, G, HS, PF, NW>(a.d, b, h, 0, 0, count, seq, page_at);
 
   if (a.update_completed && seq > 0 && seq % SP == 0) {
     constexpr int SEGS = CentroidShape<T, D>::SEGS;
@@ -83,40 +129,53 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int NW>
 hipError_t run_step(const StepArgs& a, hipStream_t s) {
   constexpr int HS = attend_head_slices<G>(), PF = attend_prefetch<T, D>();
-  const size_t lds = (2 * (size_t)a.max_pages + (size_t)a.k_tot) * sizeof(uint32_t);
-  hipLaunchKernelGGL((decode_step_kernel<T, D, G, HS, PF>), dim3(a.s.H_kv, a.s.B),
-                     dim3(kStepThreads), lds, s, a);
+  const size_t lds = step_dynamic_lds(a.max_pages, a.k_tot, a.longest_first ? a.s.B : 0);
+  hipLaunchKernelGGL((decode_step_kernel<T, D, G, HS, PF, NW>), dim3(a.s.H_kv, a.s.B),
+                     dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
+template <typename T, int D, int G>
+hipError_t run_step_w(int waves, const StepArgs& a, hipStream_t s) {
+  return waves == 4 ? run_step<T, D, G, 4>(a, s) : run_step<T, D, G, 8>(a, s);
+}
+
 template <typename T, int D>
-hipError_t run_step_g(int G, const StepArgs& a, hipStream_t s) {
+hipError_t run_step_g(int G, int waves, const StepArgs& a, hipStream_t s) {
   switch (G) {
-    case 1: return run_step<T, D, 1>(a, s);
-    case 2: return run_step<T, D, 2>(a, s);
-    case 4: return run_step<T, D, 4>(a, s);
-    case 8: return run_step<T, D, 8>(a, s);
+    case 1: return run_step_w<T, D, 1>(waves, a, s);
+    case 2: return run_step_w<T, D, 2>(waves, a, s);
+    case 4: return run_step_w<T, D, 4>(waves, a, s);
+    case 8: return run_step_w<T, D, 8>(waves, a, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+size_t step_dynamic_lds(int max_pages, int k_tot, int ordered_batch) {
+  const size_t main = 2 * (size_t)max_pages + (size_t)k_tot;
+  const size_t order = ((size_t)ordered_batch + 3) & ~(size_t)3;
+  return (main > order ? main : order) * sizeof(uint32_t);
+}
+
 bool decode_step_supported(int dtype, int D, int G) {
   return (dtype == 0 || dtype == 1) && (D == 64 || D == 128) &&
          (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
-hipError_t launch_decode_step(int dtype, int D, int G, const StepArgs& a, hipStream_t s) {
+hipError_t launch_decode_step(int dtype, int D, int G, int waves, const StepArgs& a,
+                              hipStream_t s) {
+  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
   if (dtype == 0) {
-    if (D == 64) return run_step_g<float, 64>(G, a, s);
-    if (D == 128) return run_step_g<float, 128>(G, a, s);
+    if (D == 64) return run_step_g<float, 64>(G, waves, a, s);
+    if (D == 128) return run_step_g<float, 128>(G, waves, a, s);
   } else {
-    if (D == 64) return run_step_g<bf16_t, 64>(G, a, s);
-    if (D == 128) return run_step_g<bf16_t, 128>(G, a, s);
+    if (D == 64) return run_step_g<bf16_t, 64>(G, waves, a, s);
+    if (D == 128) return run_step_g<bf16_t, 128>(G, waves, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -227,10 +227,13 @@ def run_step(vx, c: Case, q_dev, update: bool = True, ws=None):
     """vx_sparse_decode_step: returns (sel, out, lse)."""
     w = c.w
     bt = c.batch(vx)
-    sel = torch.empty((w.batch, w.num_kv_heads, w.k_tot), dtype=torch.int32, device=q_dev.device)
-    out = torch.empty((w.batch, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype,
-                      device=q_dev.device)
-    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=q_dev.device)
+    # sentinels: a row the call fails to write shows up in the comparison
+    sel = torch.full((w.batch, w.num_kv_heads, w.k_tot), -7, dtype=torch.int32,
+                     device=q_dev.device)
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim_v), float("nan"), dtype=w.torch_dtype,
+                     device=q_dev.device)
+    lse = torch.full((w.batch, w.num_q_heads), float("nan"), dtype=torch.float32,
+                     device=q_dev.device)
     if ws is None:
         ws = vx.alloc_workspace(vx.VX_OP_DECODE_STEP, c.kv, bt, w.k_tot)
     vx.sparse_decode_step(c.kv, bt, q_dev, w.topk, w.n_bos, w.n_eos, update, w.sm_scale, sel,

@@ -373,7 +373,36 @@ def test_decode_step_edge_lengths(vx, dtype, D, G, S, topk, bos, eos):
                                           synth.completed_pages(c.layout, 0)]))
 
 
-@pytest.mark.parametrize("name", ["qwen3_0p6b_b32_l32k", "long_b8_l128k", "mla_b64_l32k"])
+@pytest.mark.parametrize("batch,H_kv,G,lens", [
+    (80, 8, 2, (1, 15, 16, 17, 200, 513, 1600)),       # 4-wave blocks, longest first
+    (520, 1, 4, (1, 16, 17, 40, 64)),                   # 4-wave blocks, request order
+])
+def test_decode_step_many_units(vx, batch, H_kv, G, lens):
+    """Two or more (request, KV head) units per CU: the fused step's 4-wave
+    blocks (taken longest request first up to 512 requests, with many equal
+    lengths) write every request's row, equal to the oracle, with the same
+    selection as vx_score_topk."""
+    rng = np.random.default_rng(batch)
+    seq_lens = tuple(int(x) for x in rng.choice(lens, size=batch))
+    w = synth.Workload(name="many_units", batch=batch, num_q_heads=H_kv * G, num_kv_heads=H_kv,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, dtype="bf16", topk=6,
+                       structure="page_offset", seed=79, seq_lens=seq_lens, spare_pages=4)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    H.fix_gaps(c, range(w.batch))
+    q = c.q_host.cuda()
+    sel, out, lse = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, H.run_indexer(vx, c, q))
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel, out, lse)
+    H.assert_centroids(c, np.concatenate([synth.setup_full_pages(c.layout),
+                                          synth.completed_pages(c.layout, 0)]))
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_b32_l32k", "hetero_b128_l4k_64k", "long_b8_l128k",
+                                  "mla_b64_l32k"])
 def test_full_size_step_sampled(vx, name):
     w = synth.get_workload(name)
     _mla_guard(vx, w)
