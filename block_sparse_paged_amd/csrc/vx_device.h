@@ -119,13 +119,33 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Integer DPP move; rows not in ROW_MASK and lanes whose source lies outside
+// their row read 0.  Controls: row_shr:n = 0x110 + n, row_bcast:15 = 0x142
+// (lane 15 of each row to the next row), row_bcast:31 = 0x143 (lane 31 to
+// rows 2 and 3), plus the quad_perm / mirror controls above.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_int(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then each row adds the totals of the rows
+// below it through the two row broadcasts.
+__device__ __forceinline__ int row_inclusive_scan(int x);
+
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  x = row_inclusive_scan(x);
+  x += dpp_int<0x142, 0xA>(x);
+  x += dpp_int<0x143, 0xC>(x);
+  return x;
+}
+
+// Inclusive prefix sum within each row of 16 lanes.
+__device__ __forceinline__ int row_inclusive_scan(int x) {
+  x += dpp_int<0x111>(x);
+  x += dpp_int<0x112>(x);
+  x += dpp_int<0x114>(x);
+  x += dpp_int<0x118>(x);
   return x;
 }
 

@@ -60,6 +60,9 @@ struct DecodeArgs {
 
 // One fused decode step per (request, KV head) block: completed-page
 // centroid, indexer and attention over the selection.
+// Upper bound of the LDS one block's page selection uses (static).
+constexpr size_t kSelectLdsBytes = 12 * 1024;
+
 struct StepArgs {
   DecodeArgs d;           // attention (n_split = 1; sel unused)
   ScoreArgs s;            // indexer (scores unused)
@@ -91,6 +94,8 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 int mla_max_pages_per_split();
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
 bool decode_step_supported(int dtype, int D, int G);
+// Entries rounded up to a multiple of 4 (16-byte aligned LDS arrays).
+constexpr int round4(int n) { return (n + 3) & ~3; }
 // Dynamic LDS bytes of a fused step block; ordered_batch = B when block rows
 // go to requests longest first, else 0.
 size_t step_dynamic_lds(int max_pages, int k_tot, int ordered_batch);

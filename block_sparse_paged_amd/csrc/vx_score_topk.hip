@@ -19,11 +19,11 @@
 //         few (request, KV head) units exist (long contexts, MLA's single
 //         latent head).
 //
-// Selection (both schedules): exact top-k by an 8-bit radix select over the
-// keys (one LDS histogram per pass, every wave locating the digit itself, and
-// an early stop once the boundary bin is taken whole), equal keys ranked by
-// page, then the union with the reserved pages is compacted in ascending
-// page order with one block-wide scan.
+// Selection (both schedules): the k-th largest (key, page) pair from a
+// histogram of the key range in at most 1024 bins (every wave locating the
+// boundary bin itself), the boundary bin's keys ranked exactly (or the bin
+// histogrammed again when it holds more than 256), then the union with the
+// reserved pages compacted in ascending page order with one block-wide scan.
 #include "vx_select.h"
 
 namespace vx {
@@ -37,11 +37,9 @@ constexpr int kLoadsInFlight = 16;   // wave-loads issued before the first is us
 // ---------------------------------------------------------------- fused
 template <typename T, int D>
 __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs a, TopkArgs t) {
-  extern __shared__ uint32_t dyn[];          // phys [max_cand] then keys [max_cand]
+  extern __shared__ __align__(16) uint32_t dyn[];   // phys, keys: round4(max_cand) each
   __shared__ float qbar[D];
-  __shared__ int hist[4 * 256];
-  __shared__ int scan_tmp[kFusedThreads / 64];
-  __shared__ uint32_t bounds_tmp[2 * kFusedThreads / 64];
+  __shared__ SelectLds<kFusedThreads> sl;
 
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -51,22 +49,19 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs 
   const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
   const bool scoring = n_cand > t.topk && t.topk > 0;
   int32_t* phys = reinterpret_cast<int32_t*>(dyn);
-  uint32_t* keys = dyn + a.score_stride;
+  uint32_t* keys = dyn + round4(a.score_stride);
 
   if (scoring) {
     head_query_mean<T, D, kFusedThreads>(a, b, h, qbar);
     const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
     for (int i = tid; i < n_cand; i += kFusedThreads) phys[i] = ptb[i];
   }
-  for (int i = tid; i < 4 * 256; i += kFusedThreads) hist[i] = 0;
+  select_init<kFusedThreads>(sl);
   __syncthreads();
 
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  if (scoring) score_head<T, D, kFusedThreads>(a, h, n_cand, phys, qbar, keys, kmax, kmin);
-  block_key_bounds<kFusedThreads>(kmax, kmin, bounds_tmp);
+  if (scoring) score_head<T, D, kFusedThreads>(a, h, n_cand, phys, qbar, keys, sl);
   select_pages<kFusedThreads>(keys, n_cand, n_b, t.topk, t.n_bos, t.n_eos, t.k_tot,
-                              t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, nullptr, hist,
-                              scan_tmp, kmax, kmin);
+                              t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, nullptr, sl);
 }
 
 // ---------------------------------------------------------------- split
@@ -247,10 +242,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  extern __shared__ uint32_t keys[];        // [n_cand]
-  __shared__ int hist[4 * 256];
-  __shared__ int scan_tmp[kTopkThreads / 64];
-  __shared__ uint32_t bounds_tmp[2 * kTopkThreads / 64];
+  extern __shared__ __align__(16) uint32_t keys[];   // [round4(n_cand)]
+  __shared__ SelectLds<kTopkThreads> sl;
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;                // b * H_kv + h
@@ -259,20 +252,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
   const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  select_init<kTopkThreads>(sl);
+  __syncthreads();
   if (n_cand > a.topk && a.topk > 0) {
     const float* sc = a.scores + (size_t)bh * a.score_stride;
     for (int i = tid; i < n_cand; i += kTopkThreads) {
       const uint32_t k = order_key(sc[i]);
       keys[i] = k;
-      kmax = max(kmax, k);
-      kmin = min(kmin, k);
+      select_count<kTopkThreads>(sl, k);
     }
   }
-  for (int i = tid; i < 4 * 256; i += kTopkThreads) hist[i] = 0;
-  block_key_bounds<kTopkThreads>(kmax, kmin, bounds_tmp);
   select_pages<kTopkThreads>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
-                             a.sel + (size_t)bh * a.k_tot, nullptr, hist, scan_tmp, kmax, kmin);
+                             a.sel + (size_t)bh * a.k_tot, nullptr, sl);
 }
 
 template <typename T, int D>
@@ -284,7 +275,7 @@ hipError_t run_score(const ScoreArgs& a, int grid_x, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t run_fused(const ScoreArgs& a, const TopkArgs& t, hipStream_t s) {
-  const size_t lds = 2 * (size_t)(a.score_stride > 0 ? a.score_stride : 1) * sizeof(uint32_t);
+  const size_t lds = 2 * (size_t)round4(a.score_stride > 0 ? a.score_stride : 1) * sizeof(uint32_t);
   hipLaunchKernelGGL((indexer_fused_kernel<T, D>), dim3(a.H_kv, a.B), dim3(kFusedThreads), lds, s,
                      a, t);
   return hipGetLastError();
@@ -328,7 +319,7 @@ hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t
 }
 
 hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s) {
-  const size_t lds = (size_t)(max_cand > 0 ? max_cand : 1) * sizeof(uint32_t);
+  const size_t lds = (size_t)round4(max_cand > 0 ? max_cand : 1) * sizeof(uint32_t);
   hipLaunchKernelGGL(topk_kernel, dim3(a.B * a.H_kv), dim3(kTopkThreads), lds, s, a);
   return hipGetLastError();
 }

@@ -1,10 +1,21 @@
 // Exact page selection shared by the indexer kernels and the fused decode
-// step: order-preserving keys, an 8-bit radix select for the k-th largest
-// key, index-ordered ranking of keys equal to it (ties go to the lower
-// logical page), and the ascending union with the reserved first / last
-// pages (vortex_torch README, "Quick Example" topK and "Using Your Sparse
-// Attention with SGLang" reserved BOS / EOS pages).
+// step (vortex_torch README, "Quick Example" topK, and "Using Your Sparse
+// Attention with SGLang" reserved BOS / EOS pages): the top-k candidates by
+// score, ties to the lower logical page, unioned with the reserved first /
+// last pages and listed in ascending page order.
+//
+// Scores become order-preserving 32-bit keys.  The k-th largest (key, page)
+// pair is located by histograms: level 0 counts the keys in 1024 fixed bins
+// (the top ten key bits: sign, exponent and one mantissa bit, i.e. half an
+// octave of score) and is filled by the caller while it computes the keys;
+// each further level splits the boundary bin's key range into at most 1024
+// equal bins, until the boundary bin is taken whole or holds one key value
+// (then equal keys are taken in page order).  A candidate is taken iff
+// (key, -page) >= the threshold pair.  Every step is a few dozen
+// instructions per wave: this runs on each block's critical path.
 #pragma once
+
+#include <limits.h>
 
 #include "vx_device.h"
 #include "vx_internal.h"
@@ -16,152 +27,195 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of one int per thread over an NT-thread block, in thread
-// order.  `tmp` holds NT/64 ints of LDS.  Also returns the block total.
+constexpr int kSelBits = 10;
+constexpr int kSelBins = 1 << kSelBits;
+constexpr int kSelShift0 = 32 - kSelBits;     // level-0 bin of a key: key >> 22
+
+// Histogram slot of bin i: 4 words of padding after every 16 bins, so that
+// 16-byte reads of 16 consecutive bins by consecutive lanes spread over all
+// LDS banks.
+__device__ __forceinline__ int sel_slot(int i) { return i + (i >> 4) * 4; }
+constexpr int kSelHistWords = kSelBins + kSelBins / 4;
+
+// LDS of one selection (NT threads): two histograms (levels alternate).
 template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
+struct SelectLds {
+  alignas(16) int hist[2][kSelHistWords];
+  int wsum[2][NT / 64];
+  int misc[4];
+};
+
+static_assert(sizeof(SelectLds<512>) <= kSelectLdsBytes, "selection LDS bound");
+
+// Clears both histograms; the caller synchronises before the keys (and their
+// level-0 counts) are produced.
+template <int NT>
+__device__ __forceinline__ void select_init(SelectLds<NT>& S) {
+  int* h = &S.hist[0][0];
+  for (int i = threadIdx.x; i < 2 * kSelHistWords; i += NT) h[i] = 0;
+}
+
+// Level-0 count of one key (any thread, any time before select_pages).
+template <int NT>
+__device__ __forceinline__ void select_count(SelectLds<NT>& S, uint32_t key) {
+  atomicAdd(&S.hist[0][sel_slot((int)(key >> kSelShift0))], 1);
+}
+
+// Exclusive scan of one int per thread over an NT-thread block, in thread
+// order, through LDS `wsum` (NT/64 ints).  Also returns the block total.
+// Synchronises once; `wsum` may not be reused before the next barrier.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int inc = wave_inclusive_scan(x);
-  if (lane == 63) tmp[wave] = inc;
+  if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
-    const int t = tmp[w];
+    const int t = wsum[w];
     base += (w < wave) ? t : 0;
     tot += t;
   }
-  __syncthreads();
   *total = tot;
   return base + inc - x;
 }
 
-// Selects and writes one (request, KV head) row of `sel` (and, when
-// `lds_out` is given, the same list into LDS); returns the number of pages
-// taken.
-//   keys     LDS, n_cand order-preserving keys of candidates n_bos.. (in page order)
-//   hist     LDS, 4*256 ints, zero on entry
-// Keys and the zeroed histograms must be visible to every thread (the caller
-// synchronises first).
-//   kmax/kmin the largest / smallest key (bytes above the first byte in which
-//            they differ are common to every key, so those passes are skipped)
+// In a histogram of 1024 bins, the bin where the count from the top reaches
+// `remaining` (1 <= remaining <= total): returns the bin, the count above it
+// and its own count, the same in every lane.  Lane l first sums bins
+// 16l .. 16l + 15 to find the crossing lane, then lanes 0..15 take one bin
+// each of that lane, from the top down.
+__device__ __forceinline__ void find_bin(const int* hist, int remaining, int& dsel, int& above,
+                                         int& cnt) {
+  const int lane = threadIdx.x & 63;
+  const int4* hp = reinterpret_cast<const int4*>(hist + sel_slot(16 * lane));
+  const int4 a = hp[0], b = hp[1], c = hp[2], d = hp[3];
+  const int own = (a.x + a.y + a.z + a.w) + (b.x + b.y + b.z + b.w) +
+                  (c.x + c.y + c.z + c.w) + (d.x + d.y + d.z + d.w);
+  const int inc = wave_inclusive_scan(own);
+  const int upper = __builtin_amdgcn_readlane(inc, 63) - inc;   // keys in lanes above
+  const unsigned long long cross = __ballot(upper < remaining && upper + own >= remaining);
+  const int L = __builtin_ctzll(cross);
+  const int upL = __builtin_amdgcn_readlane(upper, L);
+  const int j = lane & 15;
+  const int hv = hist[sel_slot(16 * L + 15 - j)];
+  const int incj = row_inclusive_scan(hv);                      // bins from the top down
+  const unsigned long long hit =
+      __ballot(lane < 16 && upL + incj - hv < remaining && upL + incj >= remaining);
+  const int J = __builtin_ctzll(hit);
+  dsel = 16 * L + 15 - J;
+  above = upL + __builtin_amdgcn_readlane(incj - hv, J);
+  cnt = __builtin_amdgcn_readlane(hv, J);
+}
+
+// Selects one (request, KV head)'s pages and returns how many were taken.
+// The list goes to LDS `lds_out` when given (the caller writes the row of
+// `sel` later, so that no barrier waits on those global stores), else to
+// `out` (a row of k_tot entries, padded with -1).
+//   keys   LDS, 16-byte aligned, readable up to roundup(n_cand, 4): the
+//          order-preserving keys of candidates n_bos.. (in page order), each
+//          counted by select_count; keys and counts visible to every thread
+//   S      select_init()ed
 template <int NT>
-__device__ int select_pages(const uint32_t* keys, int n_cand, int n_b, int topk, int n_bos,
-                            int n_eos, int k_tot, int32_t* out, int32_t* lds_out, int* hist,
-                            int* scan_tmp, uint32_t kmax, uint32_t kmin) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const bool all = n_cand <= topk;
-  const bool none = !all && topk == 0;
-  uint32_t thr = 0, msk = 0;
-  int take_eq = 0, cnt_eq = 0;
-  if (!all && !none) {
-    int remaining = topk;
-    const uint32_t diff = kmax ^ kmin;
-    const int hb = diff ? 31 - __builtin_clz(diff) : 0;
-    const int first = 3 - hb / 8;
-    msk = first ? (0xFFFFFFFFu << (32 - 8 * first)) : 0u;
-    thr = kmax & msk;
-    cnt_eq = n_cand;
-    for (int pass = first; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      int* H = hist + 256 * pass;
-      for (int i = tid; i < n_cand; i += NT) {
-        const uint32_t k = keys[i];
-        if ((k & msk) == thr) atomicAdd(&H[(k >> shift) & 255u], 1);
+__device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, int n_b, int topk,
+                                            int n_bos, int n_eos, int k_tot, int32_t* out,
+                                            int32_t* lds_out, SelectLds<NT>& S) {
+  const int tid = threadIdx.x;
+  // candidate c is taken iff keys[c] > thr_key || (keys[c] == thr_key && c <= thr_idx)
+  uint32_t thr_key = 0u;
+  int thr_idx = INT_MAX;                                  // all candidates
+  if (n_cand > topk && topk == 0) {
+    thr_key = 0xFFFFFFFFu;                                // none of them
+    thr_idx = -1;
+  } else if (n_cand > topk) {
+    int remaining = topk;              // still to take from keys in [lo, lo + span]
+    uint32_t lo = 0u, span = 0xFFFFFFFFu;
+    int shift = kSelShift0;
+    for (int level = 0;; ++level) {
+      int* H = S.hist[level & 1];
+      if (level > 0) {
+        if (level > 1) {               // this buffer held level - 2
+          for (int i = tid; i < kSelHistWords; i += NT) H[i] = 0;
+          __syncthreads();
+        }
+        for (int i0 = tid; i0 < n_cand; i0 += 4 * NT) {
+          uint32_t k[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) k[j] = i0 + j * NT < n_cand ? keys[i0 + j * NT] : 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (i0 + j * NT < n_cand && k[j] - lo <= span)
+              atomicAdd(&H[sel_slot((int)((k[j] - lo) >> shift))], 1);
+        }
       }
       __syncthreads();
-      // every wave finds the bin where the count from the top crosses `remaining`
-      const int h0 = H[4 * lane], h1 = H[4 * lane + 1], h2 = H[4 * lane + 2], h3 = H[4 * lane + 3];
-      const int own = h0 + h1 + h2 + h3;
-      int suf = own;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_down(suf, d, 64);
-        if (lane + d < 64) suf += y;
-      }
-      int acc = suf - own, dsel = -1, above = 0, cnt = 0;
-      if (acc < remaining && acc + h3 >= remaining) { dsel = 4 * lane + 3; above = acc; cnt = h3; }
-      acc += h3;
-      if (dsel < 0 && acc < remaining && acc + h2 >= remaining) { dsel = 4 * lane + 2; above = acc; cnt = h2; }
-      acc += h2;
-      if (dsel < 0 && acc < remaining && acc + h1 >= remaining) { dsel = 4 * lane + 1; above = acc; cnt = h1; }
-      acc += h1;
-      if (dsel < 0 && acc < remaining && acc + h0 >= remaining) { dsel = 4 * lane; above = acc; cnt = h0; }
-      const unsigned long long found = __ballot(dsel >= 0);
-      const int src = __builtin_ctzll(found);
-      const int d = __builtin_amdgcn_readlane(dsel, src);
-      above = __builtin_amdgcn_readlane(above, src);
-      cnt = __builtin_amdgcn_readlane(cnt, src);
+      int dsel, above, cnt;
+      find_bin(H, remaining, dsel, above, cnt);
       remaining -= above;
-      thr |= (uint32_t)d << shift;
-      msk |= 0xFFu << shift;
-      cnt_eq = cnt;
-      if (remaining == cnt) break;    // the whole boundary bin is taken
+      lo += (uint32_t)dsel << shift;
+      span = min(span - ((uint32_t)dsel << shift), (1u << shift) - 1u);
+      if (remaining == cnt) {          // the whole bin is taken
+        thr_key = lo;
+        break;
+      }
+      if (span == 0) {                 // cnt equal keys: the remaining-th in page order
+        const int per = (n_cand + NT - 1) / NT;
+        const int c0 = min(tid * per, n_cand), c1 = min(c0 + per, n_cand);
+        int n_eq = 0;
+        for (int i = c0; i < c1; ++i) n_eq += keys[i] == lo ? 1 : 0;
+        int dummy;
+        int r = block_exclusive_scan<NT>(n_eq, S.wsum[0], &dummy);
+        if (r < remaining && r + n_eq >= remaining) {
+          for (int i = c0; i < c1; ++i)
+            if (keys[i] == lo && ++r == remaining) S.misc[0] = i;
+        }
+        __syncthreads();
+        thr_key = lo;
+        thr_idx = S.misc[0];
+        break;
+      }
+      const int nb = 32 - __builtin_clz(span);
+      shift = nb > kSelBits ? nb - kSelBits : 0;
     }
-    take_eq = remaining;
   }
-  const bool need_rank = !all && !none && take_eq < cnt_eq;
 
-  // thread tid owns logical pages [p_lo, p_hi)
-  const int per = (n_b + NT - 1) / NT;
-  const int p_lo = min(tid * per, n_b), p_hi = min(p_lo + per, n_b);
-  const int eos_lo = n_b - n_eos;
-  int eq_rank = 0, dummy;
-  if (need_rank) {
-    int n_eq = 0;
-    for (int p = max(p_lo, n_bos); p < min(p_hi, eos_lo); ++p) n_eq += (keys[p - n_bos] & msk) == thr;
-    eq_rank = block_exclusive_scan<NT>(n_eq, scan_tmp, &dummy);
+  // Compaction in page order: reserved first pages, taken candidates, reserved
+  // last pages.  Thread tid owns candidates [tid * per, tid * per + per),
+  // per a multiple of 4 (16-byte key reads).
+  int per = (n_cand + NT - 1) / NT;
+  per = (per + 3) & ~3;
+  const int c0 = tid * per;
+  int n_take = 0;
+  for (int c = c0; c < c0 + per && c < n_cand; c += 4) {
+    const uint4 kv = *reinterpret_cast<const uint4*>(keys + c);
+    const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      n_take += (c + e < n_cand && (k4[e] > thr_key || (k4[e] == thr_key && c + e <= thr_idx)))
+                    ? 1 : 0;
   }
-  auto take = [&](int p, int& rank) -> bool {
-    if (p < n_bos || p >= eos_lo) return true;
-    if (all || none) return all;
-    const uint32_t km = keys[p - n_bos] & msk;
-    bool t = km > thr;
-    if (km == thr) {
-      t = !need_rank || rank < take_eq;
-      ++rank;
-    }
-    return t;
-  };
-  int r = eq_rank, n_take = 0;
-  for (int p = p_lo; p < p_hi; ++p) n_take += take(p, r) ? 1 : 0;
-  int total;
-  int pos = block_exclusive_scan<NT>(n_take, scan_tmp, &total);
-  r = eq_rank;
-  for (int p = p_lo; p < p_hi; ++p)
-    if (take(p, r)) {
-      out[pos] = p;
-      if (lds_out) lds_out[pos] = p;
-      ++pos;
-    }
-  for (int i = total + tid; i < k_tot; i += NT) out[i] = -1;
+  int taken;
+  int pos = block_exclusive_scan<NT>(n_take, S.wsum[1], &taken);
+  const int n_lo = n_cand > 0 ? n_bos : n_b;           // no candidates: every page is reserved
+  const int n_hi = n_cand > 0 ? n_eos : 0;
+  const int total = n_lo + taken + n_hi;
+  int32_t* dst = lds_out ? lds_out : out;
+  pos += n_lo;
+  for (int c = c0; c < c0 + per && c < n_cand; c += 4) {
+    const uint4 kv = *reinterpret_cast<const uint4*>(keys + c);
+    const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c + e < n_cand && (k4[e] > thr_key || (k4[e] == thr_key && c + e <= thr_idx)))
+        dst[pos++] = n_bos + c + e;
+  }
+  for (int i = tid; i < n_lo; i += NT) dst[i] = i;
+  for (int i = tid; i < n_hi; i += NT) dst[n_lo + taken + i] = n_b - n_eos + i;
+  if (!lds_out)
+    for (int i = total + tid; i < k_tot; i += NT) out[i] = -1;
   return total;
 }
-
-// Block-wide max and min of per-thread key bounds (NT threads, LDS `tmp` of
-// 2 * NT/64 words).  Synchronises.
-template <int NT>
-__device__ __forceinline__ void block_key_bounds(uint32_t& kmax, uint32_t& kmin, uint32_t* tmp) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, 64));
-  }
-  if (lane == 0) {
-    tmp[wave] = kmax;
-    tmp[NT / 64 + wave] = kmin;
-  }
-  __syncthreads();
-  kmax = 0u;
-  kmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    kmax = max(kmax, tmp[w]);
-    kmin = min(kmin, tmp[NT / 64 + w]);
-  }
-}
-
 
 // Group-mean query of KV head h of request b into LDS `qbar` (fp32, heads
 // summed in order).  Every thread of the NT-thread block takes part.
@@ -197,15 +251,16 @@ __device__ __forceinline__ void head_query_mean(const ScoreArgs& a, int b, int h
 }
 
 // Scores of candidates [0, n_cand) of KV head h into LDS `keys` as
-// order-preserving keys; phys[c] is candidate c's physical page.  Rows are
-// one head's centroid row (<= 64 lanes of 16 bytes); each wave keeps
-// kScoreLoads wave-loads in flight.  Also tracks the thread's key bounds.
+// order-preserving keys, each counted into the selection's level-0
+// histogram; phys[c] is candidate c's physical page.  Rows are one head's
+// centroid row (<= 64 lanes of 16 bytes); each wave keeps kScoreLoads
+// wave-loads in flight.
 constexpr int kScoreLoads = 16;
 
 template <typename T, int D, int NT>
 __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand,
                                            const int32_t* phys, const float* qbar,
-                                           uint32_t* keys, uint32_t& kmax, uint32_t& kmin) {
+                                           uint32_t* keys, SelectLds<NT>& S) {
   using V = Vec16<T>;
   constexpr int E = V::E;
   constexpr int LH = D / E;                  // lanes per centroid row
@@ -237,11 +292,10 @@ __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand
 #pragma unroll
       for (int e = 0; e < E; ++e) acc = fmaf(qr[e], f[e], acc);
       acc = lane_group_sum<LH>(acc);
-      if (c < n_cand) {
+      if (c < n_cand && seg == 0) {
         const uint32_t k = order_key(acc);
-        kmax = max(kmax, k);
-        kmin = min(kmin, k);
-        if (seg == 0) keys[c] = k;
+        keys[c] = k;
+        select_count<NT>(S, k);
       }
     }
   }

@@ -6,7 +6,8 @@
 //   1. stage the request's page-table row and the head's group-mean query
 //      in LDS;
 //   2. score every candidate page's centroid (order-preserving keys in LDS);
-//   3. select top-k + reserved pages (written to `sel` and kept in LDS);
+//   3. select top-k + reserved pages (kept in LDS; the row of `sel` is
+//      stored at the end);
 //   4. attend over the selected pages (K/V loads start as soon as the list
 //      exists: physical pages come from the staged row, no HBM round trip);
 //   5. if the token completed a page, write that page's centroid row for
@@ -39,7 +40,7 @@ namespace {
 // decreasing length, ties to the lower index: the request whose rank is r.
 // len: LDS of roundup(B, 4) ints; pick: one LDS int.  Synchronises.
 template <int NT>
-__device__ int longest_first_request(const int32_t* seq_lens, int B, int max_tokens, int r,
+__device__ __forceinline__ int longest_first_request(const int32_t* seq_lens, int B, int max_tokens, int r,
                                      int* len, int* pick) {
   const int tid = threadIdx.x;
   const int B4 = (B + 3) & ~3;
@@ -69,11 +70,9 @@ __device__ int longest_first_request(const int32_t* seq_lens, int B, int max_tok
 template <typename T, int D, int G, int HS, int PF, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   constexpr int NT = NW * 64;
-  extern __shared__ __align__(16) uint32_t dyn[];   // page row [max_pages], keys [max_pages], list [k_tot]
+  extern __shared__ __align__(16) uint32_t dyn[];   // page row, keys (each round4(max_pages)), list [k_tot]
   __shared__ float qbar[D];
-  __shared__ int hist[4 * 256];
-  __shared__ int scan_tmp[NW];
-  __shared__ uint32_t bounds_tmp[2 * NW];
+  __shared__ SelectLds<NT> sl;
 
   __shared__ int pick;
 
@@ -91,21 +90,18 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
   const bool scoring = n_cand > a.topk && a.topk > 0;
   int32_t* prow = reinterpret_cast<int32_t*>(dyn);
-  uint32_t* keys = dyn + a.max_pages;
-  int32_t* list = reinterpret_cast<int32_t*>(dyn + 2 * a.max_pages);
+  uint32_t* keys = dyn + round4(a.max_pages);
+  int32_t* list = reinterpret_cast<int32_t*>(dyn + 2 * round4(a.max_pages));
 
   const int32_t* ptb = s.pt + (size_t)b * s.pt_stride;
   for (int i = tid; i < n_b; i += NT) prow[i] = ptb[i];
   if (scoring) head_query_mean<T, D, NT>(s, b, h, qbar);
-  for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0;
+  select_init<NT>(sl);
   __syncthreads();
 
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  if (scoring) score_head<T, D, NT>(s, h, n_cand, prow + a.n_bos, qbar, keys, kmax, kmin);
-  block_key_bounds<NT>(kmax, kmin, bounds_tmp);
-  const int count = select_pages<NT>(
-      keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
-      a.sel + ((size_t)b * s.H_kv + h) * a.k_tot, list, hist, scan_tmp, kmax, kmin);
+  if (scoring) score_head<T, D, NT>(s, h, n_cand, prow + a.n_bos, qbar, keys, sl);
+  const int count = select_pages<NT>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
+                                     nullptr, list, sl);
   __syncthreads();
 
   auto page_at = [&](int idx, bool active) -> int2 {
@@ -117,6 +113,10 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
     return make_int2(logi, phys);
   };
   attend_pages<T, D, G, HS, PF, NW>(a.d, b, h, 0, 0, count, seq, page_at);
+
+  // the row of `sel`, stored only now so that no barrier above waits on it
+  int32_t* srow = a.sel + ((size_t)b * s.H_kv + h) * a.k_tot;
+  for (int i = tid; i < a.k_tot; i += NT) srow[i] = i < count ? list[i] : -1;
 
   if (a.update_completed && seq > 0 && seq % SP == 0) {
     constexpr int SEGS = CentroidShape<T, D>::SEGS;
@@ -157,7 +157,7 @@ hipError_t run_step_g(int G, int waves, const StepArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t step_dynamic_lds(int max_pages, int k_tot, int ordered_batch) {
-  const size_t main = 2 * (size_t)max_pages + (size_t)k_tot;
+  const size_t main = 2 * (size_t)round4(max_pages) + (size_t)k_tot;
   const size_t order = ((size_t)ordered_batch + 3) & ~(size_t)3;
   return (main > order ? main : order) * sizeof(uint32_t);
 }

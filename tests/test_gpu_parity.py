@@ -418,3 +418,81 @@ def test_full_size_step_sampled(vx, name):
         H.log(f"  request {b}")
         _check_request(vx, c, b, sel, out, lse)
     H.assert_centroids(c, synth.completed_pages(c.layout, 0))
+
+
+@pytest.mark.parametrize("classes,topk", [(1, 30), (7, 20), (7, 150), (3, 400)])
+def test_selection_with_exact_ties(vx, classes, topk):
+    """Every page of a request is a copy of one of `classes` K tiles, so the
+    centroid scores take `classes` distinct values and the top-k boundary
+    falls inside a class of exactly equal scores (with one class, inside
+    more than a thousand equal keys).  Ties must go to the lower pages, in the
+    indexer and in the fused step alike."""
+    lens = (16 * 1200 + 5, 16 * 300, 16 * 40 + 1)
+    w = synth.Workload(name="ties", batch=len(lens), num_q_heads=4, num_kv_heads=2,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, dtype="bf16", topk=topk,
+                       structure="gauss", seed=80, seq_lens=lens, spare_pages=2)
+    H.log(f"case {H.describe(w)} classes={classes}")
+    c = H.setup_case(vx, w)
+    for b in range(w.batch):
+        n = c.n_pages(b)
+        phys = c.pt[b, :n].long()
+        tiles = c.K[phys[:classes]].clone()
+        c.K[phys] = tiles[torch.arange(n, device=phys.device) % classes]
+    H.build_centroids(vx, c)
+    # distinct class scores must be far apart (equal ones are exactly equal)
+    G = w.group
+    for b in range(w.batch):
+        cand = orc.candidate_pages(c.n_pages(b), w.n_bos, w.n_eos)
+        cent = c.oracle_centroids(b)
+        for h in range(w.num_kv_heads):
+            qbar = orc.group_mean_query(c.q_host[b, h * G:(h + 1) * G].double().numpy(), 1)
+            vals = np.unique(orc.page_scores(qbar, cent[:, h:h + 1], cand)[0])
+            if len(vals) > 1:
+                assert np.diff(vals).min() > H.GAP_REL * np.abs(vals).max()
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    out, lse = H.run_sparse(vx, c, q, sel)
+    sel2, out2, lse2 = H.run_step(vx, c, q, update=False)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel, out, lse)
+        _check_request(vx, c, b, sel2, out2, lse2)
+
+
+def test_selection_refines_crowded_bin(vx):
+    """Scores set exactly: every query head is e0 + 2^-8 e1 + 2^-16 e2 and the
+    rows of page j carry three bf16 digits of a 24-bit integer m_j in dims
+    0..2, so the score is m_j * 2^-23 in fp32 and fp64 alike.  Hundreds of
+    distinct scores in [1, 1.0625) (some repeated) sit beside a few pages
+    scoring -64: over that key range a first histogram pass puts the whole
+    band into one or two bins, which the selection has to histogram again."""
+    lens = (16 * 900 + 3, 16 * 500)
+    w = synth.Workload(name="crowded", batch=len(lens), num_q_heads=4, num_kv_heads=2,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, dtype="bf16", topk=300,
+                       structure="gauss", seed=81, seq_lens=lens, spare_pages=2)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    rng = np.random.default_rng(81)
+    for b in range(w.batch):
+        n = c.n_pages(b)
+        phys = c.pt[b, :n].long()
+        m = rng.integers(2 ** 23, 2 ** 23 + 2 ** 19, size=(n, w.num_kv_heads))
+        m[::7] = m[3]                                        # exact repeats
+        digits = np.stack([(m >> 16), (m >> 8) & 255, m & 255], axis=-1) * 2.0 ** -7
+        out_pages = rng.choice(np.arange(1, n - 1), size=5, replace=False)
+        digits[out_pages] = [-64.0, 0.0, 0.0]
+        d = torch.from_numpy(digits).to(w.torch_dtype).to(c.K.device)     # [n, H_kv, 3]
+        assert torch.equal(d.double().cpu(), torch.from_numpy(digits))     # exact in bf16
+        c.K[phys, :, :, 0:3] = d[:, :, None, :].expand(n, w.num_kv_heads, w.page_size, 3)
+    qv = torch.zeros(w.head_dim_qk, dtype=torch.float64)
+    qv[0], qv[1], qv[2] = 1.0, 2.0 ** -8, 2.0 ** -16
+    c.q_host[:] = qv.to(w.torch_dtype)
+    H.build_centroids(vx, c)
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    out, lse = H.run_sparse(vx, c, q, sel)
+    sel2, out2, lse2 = H.run_step(vx, c, q, update=False)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel, out, lse)
+        _check_request(vx, c, b, sel2, out2, lse2)
