@@ -34,6 +34,38 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------- traffic
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def _source_sha256():
+    """Hash of the kernel sources and the C header (names and bytes)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(_ROOT, "block_sparse_paged_amd", "csrc", "*")))
+    files.append(os.path.join(_ROOT, "include", "vx.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the fused step from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record of this workload, or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(_ROOT, "profiles", f"decode_step_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != _source_sha256():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
 # ---------------------------------------------------------------- bytes
 def _pages(L, S):
     return -(-int(L) // S)
@@ -364,7 +396,9 @@ def main():
         "speedup_vs_dense": (dense["ms_per_step"] / ms_per_step) if dense else None,
         "roofline": {"bound": "hbm", "kernel": "vx_sparse_decode_step",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)"},
         "cpu_baseline": cpu,
         "algorithmic_bytes_per_step": int(b_step),
         "launch_ms_avg_over_timed_region": call_ms,
