@@ -11,8 +11,10 @@
 //   4. attend over the selected pages (K/V loads start as soon as the list
 //      exists: physical pages come from the staged row, no HBM round trip);
 //   5. if the token completed a page, write that page's centroid row for
-//      this head (the page is the last, reserved one, so no block of this
-//      step reads it; its K tile was just streamed and sits in L2).
+//      this head (the page is the last, reserved one, so no score of this
+//      step reads it).  Its K tile is loaded before the scoring loop and
+//      reduced per row group after it, so the loads cost no extra round
+//      trip; the row groups are added at the end.
 //
 // Steps 2-3 and 4 are the code of vx_score_topk's per-(request, KV head)
 // kernel and of vx_sparse_paged_decode's attention, and step 5 uses the
@@ -73,6 +75,7 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t dyn[];   // page row, keys (each round4(max_pages)), list [k_tot]
   __shared__ float qbar[D];
   __shared__ SelectLds<NT> sl;
+  __shared__ float cred[CentroidShape<T, D>::RG][D];     // completed page: row-group sums
 
   __shared__ int pick;
 
@@ -99,7 +102,49 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   select_init<NT>(sl);
   __syncthreads();
 
+  // The page this step's token completed: its K tile rows are loaded now and
+  // summed per row group after the scoring loop (the loads complete under
+  // the scoring's), the groups are added at the end.
+  using CS = CentroidShape<T, D>;
+  constexpr int CP = (CS::THREADS + NT - 1) / NT;        // (row group, segment) pairs per thread
+  constexpr int CR = 64 / CS::RG;                        // rows per pair, S_p <= 64
+  const bool upd = a.update_completed && seq > 0 && seq % SP == 0;
+  uint4 crow[CP][CR];
+  if (upd) {
+    const T* tile = reinterpret_cast<const T*>(a.d.k) + ((size_t)prow[n_b - 1] * s.H_kv + h) * SP * D;
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      const int pr = tid + c * NT, g = pr / CS::SEGS, sg = pr % CS::SEGS;
+#pragma unroll
+      for (int j = 0; j < CR; ++j)
+        if (pr < CS::THREADS && g + j * CS::RG < SP)
+          crow[c][j] = ld16(tile + (size_t)(g + j * CS::RG) * D + sg * CS::E);
+    }
+  }
+
   if (scoring) score_head<T, D, NT>(s, h, n_cand, prow + a.n_bos, qbar, keys, sl);
+  if (upd) {
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      const int pr = tid + c * NT, g = pr / CS::SEGS, sg = pr % CS::SEGS;
+      if (pr < CS::THREADS) {
+        float part[CS::E];
+#pragma unroll
+        for (int e = 0; e < CS::E; ++e) part[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < CR; ++j) {
+          if (g + j * CS::RG < SP) {
+            float f[CS::E];
+            Vec16<T>::unpack(crow[c][j], f);
+#pragma unroll
+            for (int e = 0; e < CS::E; ++e) part[e] += f[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < CS::E; ++e) cred[g][sg * CS::E + e] = part[e];
+      }
+    }
+  }
   const int count = select_pages<NT>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
                                      nullptr, list, sl);
   __syncthreads();
@@ -118,14 +163,19 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   int32_t* srow = a.sel + ((size_t)b * s.H_kv + h) * a.k_tot;
   for (int i = tid; i < a.k_tot; i += NT) srow[i] = i < count ? list[i] : -1;
 
-  if (a.update_completed && seq > 0 && seq % SP == 0) {
-    constexpr int SEGS = CentroidShape<T, D>::SEGS;
-    if (tid < SEGS) {
-      const int phys = prow[n_b - 1];
-      const T* tile = reinterpret_cast<const T*>(a.d.k) + ((size_t)phys * s.H_kv + h) * SP * D;
-      T* cp = reinterpret_cast<T*>(a.cent) + ((size_t)phys * s.H_kv + h) * D;
-      st16(cp + tid * Vec16<T>::E, centroid_segment<T, D>(tile, SP, tid));
-    }
+  if (upd && tid < CS::SEGS) {
+    // row groups added in order, then the scale: the order of centroid_segment()
+    float sum[CS::E];
+#pragma unroll
+    for (int e = 0; e < CS::E; ++e) sum[e] = 0.f;
+    for (int g = 0; g < CS::RG; ++g)
+#pragma unroll
+      for (int e = 0; e < CS::E; ++e) sum[e] += cred[g][tid * CS::E + e];
+    const float inv = 1.0f / (float)SP;
+#pragma unroll
+    for (int e = 0; e < CS::E; ++e) sum[e] *= inv;
+    T* cp = reinterpret_cast<T*>(a.cent) + ((size_t)prow[n_b - 1] * s.H_kv + h) * D;
+    st16(cp + tid * CS::E, Vec16<T>::pack(sum));
   }
 }
 
