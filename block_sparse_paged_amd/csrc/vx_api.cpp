@@ -308,7 +308,11 @@ size_t step_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
 // per page each) and the selected list; plus its static arrays.
 size_t step_lds_bytes(int max_pages, int k_tot, int D, int G, int ordered_batch) {
   const size_t dyn = step_dynamic_lds(max_pages, k_tot, ordered_batch);
-  const size_t stat = (size_t)D * 4 + kSelectLdsBytes + 8 * (size_t)G * (D + 2) * 4 + 16 * (size_t)D * 4 + 16;
+  // attention: per-wave partials (VALU form) or per-wave V staging / partials (MFMA form)
+  const size_t att_valu = 8 * (size_t)G * (D + 2) * 4;
+  const size_t att_mfma = 8 * std::max((size_t)16 * (2 * D + 32), (size_t)G * D * 4) + 2 * 8 * (size_t)G * 4;
+  const size_t stat = (size_t)D * 4 + kSelectLdsBytes + std::max(att_valu, att_mfma) +
+                      16 * (size_t)D * 4 + 16;
   return dyn + stat;
 }
 

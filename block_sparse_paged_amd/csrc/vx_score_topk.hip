@@ -86,34 +86,46 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int nc = c1 - c0;
   const int tid = threadIdx.x;
 
-  // group-mean query of every KV head, fp32, summed in head order; one
-  // 16-byte segment of one head per thread
+  // group-mean query of every KV head, fp32: thread (chunk, head, segment)
+  // sums eight query heads in order, the chunks' partials are then added in
+  // chunk order (one round of loads for any G <= 8 * 512 / (H_kv * LH))
   const int G = a.H_q / a.H_kv;
+  const int NCH = (G + 7) / 8;
+  const int QS = a.H_kv * LH;                 // (head, segment) pairs
   const T* qb = reinterpret_cast<const T*>(a.q) + (size_t)b * a.H_q * D;
   const float invG = 1.0f / (float)G;
-  for (int i = tid; i < a.H_kv * LH; i += kScoreThreads) {
-    const int h = i / LH, sg = i - h * LH;
+  float* qpart = reinterpret_cast<float*>(phys + a.cand_per_block);   // [NCH][H_kv * D] when NCH > 1
+  for (int i = tid; i < QS * NCH; i += kScoreThreads) {
+    const int ch = i / QS, hs = i - ch * QS;
+    const int h = hs / LH, sg = hs - h * LH;
+    const int g0 = ch * 8;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    // eight heads' loads in flight at a time, summed in head order
-    for (int g0 = 0; g0 < G; g0 += 8) {
-      uint4 v[8];
+    uint4 v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (g0 + j < G) v[j] = ld16(qb + (size_t)(h * G + g0 + j) * D + sg * E);
+    for (int j = 0; j < 8; ++j)
+      if (g0 + j < G) v[j] = ld16(qb + (size_t)(h * G + g0 + j) * D + sg * E);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (g0 + j < G) {
-          float f[E];
-          V::unpack(v[j], f);
+    for (int j = 0; j < 8; ++j) {
+      if (g0 + j < G) {
+        float f[E];
+        V::unpack(v[j], f);
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[e] += f[e];
-        }
+        for (int e = 0; e < E; ++e) acc[e] += f[e];
       }
     }
+    float* dst = NCH == 1 ? qbar : qpart + (size_t)ch * a.H_kv * D;
 #pragma unroll
-    for (int e = 0; e < E; ++e) qbar[h * D + sg * E + e] = acc[e] * invG;
+    for (int e = 0; e < E; ++e) dst[h * D + sg * E + e] = NCH == 1 ? acc[e] * invG : acc[e];
+  }
+  if (NCH > 1) {
+    __syncthreads();
+    for (int i = tid; i < a.H_kv * D; i += kScoreThreads) {
+      float x = 0.f;
+      for (int ch = 0; ch < NCH; ++ch) x += qpart[(size_t)ch * a.H_kv * D + i];
+      qbar[i] = x * invG;
+    }
   }
   const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
   for (int i = tid; i < nc; i += kScoreThreads) phys[i] = ptb[c0 + i];
@@ -196,6 +208,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         tl.tb = make_uint4(0, 0, 0, 0);
       }
     };
+    // with one KV head (MLA) the query segments a lane needs stay in registers
+    const bool one_head = a.H_kv == 1;
+    float qh1[E], qt1[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      qh1[e] = qbar[lane * E + e];
+      qt1[e] = qbar[(64 + lane % TL) * E + e];
+    }
     auto consume = [&](int r0, const Tile& tl) {
       const int tr = r0 + lane / TL, tseg = 64 + lane % TL;
       float tp;
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         const float* qh = qbar + h * D + tseg * E;
         tp = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) tp = fmaf(qh[e], f[e], tp);
+        for (int e = 0; e < E; ++e) tp = fmaf(one_head ? qt1[e] : qh[e], f[e], tp);
         tp = row_sum<TL>(tp);               // sum over the TL lanes of one row
       }
 #pragma unroll
@@ -220,7 +240,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         const float* qh = qbar + h * D + lane * E;
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc = fmaf(qh[e], f[e], acc);
+        for (int e = 0; e < E; ++e) acc = fmaf(one_head ? qh1[e] : qh[e], f[e], acc);
         acc = lane_group_sum<64>(acc) +
               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tp), i * TL));
         if (lane == 0 && r < rows) out[(size_t)h * a.score_stride + c0 + c] = acc;
@@ -255,11 +275,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   select_init<kTopkThreads>(sl);
   __syncthreads();
   if (n_cand > a.topk && a.topk > 0) {
+    // eight scores per thread in flight, then converted and counted
     const float* sc = a.scores + (size_t)bh * a.score_stride;
-    for (int i = tid; i < n_cand; i += kTopkThreads) {
-      const uint32_t k = order_key(sc[i]);
-      keys[i] = k;
-      select_count<kTopkThreads>(sl, k);
+    for (int i0 = tid; i0 < n_cand; i0 += 8 * kTopkThreads) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + j * kTopkThreads;
+        v[j] = i < n_cand ? sc[i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + j * kTopkThreads;
+        if (i < n_cand) {
+          const uint32_t k = order_key(v[j]);
+          keys[i] = k;
+          select_count<kTopkThreads>(sl, k);
+        }
+      }
     }
   }
   select_pages<kTopkThreads>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
@@ -268,7 +301,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
 template <typename T, int D>
 hipError_t run_score(const ScoreArgs& a, int grid_x, hipStream_t s) {
-  const size_t lds = (size_t)a.H_kv * D * sizeof(float) + (size_t)a.cand_per_block * sizeof(int32_t);
+  const int G = a.H_q / a.H_kv, nch = (G + 7) / 8;
+  const size_t lds = (size_t)a.H_kv * D * sizeof(float) + (size_t)a.cand_per_block * sizeof(int32_t) +
+                     (nch > 1 ? (size_t)nch * a.H_kv * D * sizeof(float) : 0);
   hipLaunchKernelGGL((score_kernel<T, D>), dim3(grid_x, a.B), dim3(kScoreThreads), lds, s, a);
   return hipGetLastError();
 }
