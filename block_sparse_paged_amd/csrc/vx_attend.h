@@ -206,10 +206,10 @@ __device__ __forceinline__ void attend_pages_valu(const DecodeArgs& a, int b, in
   }
 }
 
-// ---------------------------------------------------------------- MFMA (bf16, G >= 4)
-// The same attention with both products on matrix cores, for query groups of
-// four or more heads, where the VALU form issues about 30 instructions per
-// byte of K/V.  Each wave takes the list's pages round-robin like the VALU
+// ---------------------------------------------------------------- MFMA (bf16, G >= 2)
+// The same attention with both products on matrix cores, for bf16 query
+// groups of two or more heads (the VALU form issues about 8 G instructions
+// per 16-byte segment of K/V and, from G = 4 on, runs out of issue slots).  Each wave takes the list's pages round-robin like the VALU
 // form and runs one online softmax for all G heads over 16-token chunks:
 //   S^T[16 tok x 16 heads] = K Q^T  on mfma_f32_16x16x32_bf16 (D/32 k-steps):
 //     K rows come from HBM straight into the A operand (lane l: token l%16,
@@ -236,7 +236,7 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
   constexpr int PF = 2;                   // chunks of K and V in flight per wave
   constexpr int VROW = 2 * D + 32;        // LDS row stride of a V chunk (bytes)
   constexpr int VL = (16 * 2 * D) / (64 * 16);   // 16-byte V loads per lane per chunk
-  static_assert(G >= 4 && G <= 16 && D % 32 == 0, "shape");
+  static_assert(G >= 2 && G <= 16 && D % 32 == 0, "shape");
   static_assert(VL * 64 * 16 == 16 * 2 * D, "V chunk copy");
   constexpr int VBUF = 16 * VROW;
   constexpr int OBUF = G * D * 4;
@@ -421,7 +421,7 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
 // Whether a shape takes the MFMA form.
 template <typename T, int D, int G>
 constexpr bool attend_uses_mfma() {
-  return sizeof(T) == 2 && G >= 4 && (D == 64 || D == 128);
+  return sizeof(T) == 2 && G >= 2 && (D == 64 || D == 128);
 }
 
 template <typename T, int D, int G, int HS, int PF, int NW, class PageAt>
