@@ -25,9 +25,10 @@ constexpr int kNW = 8;       // waves per attention block of the split-K decode
 // page_at(idx) returns {logical page, physical page} of list entry idx; it is
 // called by every lane (inactive lanes pass active = false and get ignored).
 // NW is the block's wave count.
-template <typename T, int D, int G, int HS, int PF, int NW, class PageAt>
+template <typename T, int D, int G, int HS, int PF, int NW, class PageAt, class Epi>
 __device__ __forceinline__ void attend_pages_valu(const DecodeArgs& a, int b, int h, int split,
-                                                  int p0, int p1, int seq, PageAt page_at) {
+                                                  int p0, int p1, int seq, PageAt page_at,
+                                                  Epi epi) {
   using V = Vec16<T>;
   constexpr int E = V::E;
   constexpr int L = D / E;          // lanes per token row
@@ -174,6 +175,9 @@ __device__ __forceinline__ void attend_pages_valu(const DecodeArgs& a, int b, in
     }
   }
   __syncthreads();
+  if constexpr (G * D < NW * 64) {
+    if (tid >= G * D) epi(tid - G * D, NW * 64 - G * D);
+  }
 
   const bool direct = a.n_split == 1;
   for (int i = tid; i < G * D; i += NW * 64) {
@@ -204,6 +208,7 @@ __device__ __forceinline__ void attend_pages_valu(const DecodeArgs& a, int b, in
       }
     }
   }
+  if constexpr (G * D >= NW * 64) epi(tid, NW * 64);
 }
 
 // ---------------------------------------------------------------- MFMA (bf16, G >= 2)
@@ -225,9 +230,10 @@ __device__ __forceinline__ void attend_pages_valu(const DecodeArgs& a, int b, in
 // Results: the same (m, l, o) per head as the VALU form, merged across waves
 // the same way; only the rounding differs (P enters the product in bf16, the
 // denominator sums the fp32 weights; MFMA summation order).
-template <int D, int G, int NW, class PageAt>
+template <int D, int G, int NW, class PageAt, class Epi>
 __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, int h, int split,
-                                                  int p0, int p1, int seq, PageAt page_at) {
+                                                  int p0, int p1, int seq, PageAt page_at,
+                                                  Epi epi) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -388,6 +394,9 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
     }
   }
   __syncthreads();
+  if constexpr (G * D < NW * 64) {
+    if (tid >= G * D) epi(tid - G * D, NW * 64 - G * D);
+  }
 
   const bool direct = a.n_split == 1;
   for (int i = tid; i < G * D; i += NW * 64) {
@@ -416,6 +425,7 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
       }
     }
   }
+  if constexpr (G * D >= NW * 64) epi(tid, NW * 64);
 }
 
 // Whether a shape takes the MFMA form.
@@ -424,13 +434,21 @@ constexpr bool attend_uses_mfma() {
   return sizeof(T) == 2 && G >= 2 && (D == 64 || D == 128);
 }
 
-template <typename T, int D, int G, int HS, int PF, int NW, class PageAt>
+// Work a caller hands to the attention's merge phase: epi(t, nt) runs once
+// per thread t < nt of a thread group that is otherwise idle there (after
+// the barrier that ends the page loop), or on every thread after the merge.
+struct NoEpilogue {
+  __device__ void operator()(int, int) const {}
+};
+
+template <typename T, int D, int G, int HS, int PF, int NW, class PageAt, class Epi = NoEpilogue>
 __device__ __forceinline__ void attend_pages(const DecodeArgs& a, int b, int h, int split,
-                                             int p0, int p1, int seq, PageAt page_at) {
+                                             int p0, int p1, int seq, PageAt page_at,
+                                             Epi epi = Epi()) {
   if constexpr (attend_uses_mfma<T, D, G>())
-    attend_pages_mfma<D, G, NW>(a, b, h, split, p0, p1, seq, page_at);
+    attend_pages_mfma<D, G, NW>(a, b, h, split, p0, p1, seq, page_at, epi);
   else
-    attend_pages_valu<T, D, G, HS, PF, NW>(a, b, h, split, p0, p1, seq, page_at);
+    attend_pages_valu<T, D, G, HS, PF, NW>(a, b, h, split, p0, p1, seq, page_at, epi);
 }
 
 // Chunks of K and V kept in flight per wave: two, or one where 32 lanes per

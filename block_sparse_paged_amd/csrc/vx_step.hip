@@ -157,26 +157,27 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
     }
     return make_int2(logi, phys);
   };
-  attend_pages<T, D, G, HS, PF, NW>(a.d, b, h, 0, 0, count, seq, page_at);
-
-  // the row of `sel`, stored only now so that no barrier above waits on it
+  // the row of `sel` and the completed page's centroid, by threads the
+  // attention's merge leaves idle (stored late, so no barrier waits on them)
   int32_t* srow = a.sel + ((size_t)b * s.H_kv + h) * a.k_tot;
-  for (int i = tid; i < a.k_tot; i += NT) srow[i] = i < count ? list[i] : -1;
-
-  if (upd && tid < CS::SEGS) {
-    // row groups added in order, then the scale: the order of centroid_segment()
-    float sum[CS::E];
+  auto epilogue = [&](int t, int nt) {
+    for (int i = t; i < a.k_tot; i += nt) srow[i] = i < count ? list[i] : -1;
+    if (upd && t < CS::SEGS) {
+      // row groups added in order, then the scale: the order of centroid_segment()
+      float sum[CS::E];
 #pragma unroll
-    for (int e = 0; e < CS::E; ++e) sum[e] = 0.f;
-    for (int g = 0; g < CS::RG; ++g)
+      for (int e = 0; e < CS::E; ++e) sum[e] = 0.f;
+      for (int g = 0; g < CS::RG; ++g)
 #pragma unroll
-      for (int e = 0; e < CS::E; ++e) sum[e] += cred[g][tid * CS::E + e];
-    const float inv = 1.0f / (float)SP;
+        for (int e = 0; e < CS::E; ++e) sum[e] += cred[g][t * CS::E + e];
+      const float inv = 1.0f / (float)SP;
 #pragma unroll
-    for (int e = 0; e < CS::E; ++e) sum[e] *= inv;
-    T* cp = reinterpret_cast<T*>(a.cent) + ((size_t)prow[n_b - 1] * s.H_kv + h) * D;
-    st16(cp + tid * CS::E, Vec16<T>::pack(sum));
-  }
+      for (int e = 0; e < CS::E; ++e) sum[e] *= inv;
+      T* cp = reinterpret_cast<T*>(a.cent) + ((size_t)prow[n_b - 1] * s.H_kv + h) * D;
+      st16(cp + t * CS::E, Vec16<T>::pack(sum));
+    }
+  };
+  attend_pages<T, D, G, HS, PF, NW>(a.d, b, h, 0, 0, count, seq, page_at, epilogue);
 }
 
 template <typename T, int D, int G, int NW>
