@@ -86,6 +86,18 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
                     ? longest_first_request<NT>(s.seq_lens, s.B, s.max_tokens, blockIdx.y,
                                                 reinterpret_cast<int*>(dyn), &pick)
                     : blockIdx.y;
+  // The first page-table entries (within the batch's page bound, which the
+  // row holds) and the query are loaded before the request's length is
+  // known, so the prologue costs one memory latency, not two.
+  const int32_t* ptb = s.pt + (size_t)b * s.pt_stride;
+  constexpr int kSpec = 4;
+  int pv[kSpec];
+#pragma unroll
+  for (int j = 0; j < kSpec; ++j) {
+    const int i = tid + j * NT;
+    pv[j] = i < a.max_pages ? ptb[i] : 0;
+  }
+  head_query_mean<T, D, NT>(s, b, h, qbar);
   int seq = s.seq_lens[b];
   seq = seq < 0 ? 0 : (seq > s.max_tokens ? s.max_tokens : seq);
   const int SP = s.S_p;
@@ -96,9 +108,12 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   uint32_t* keys = dyn + round4(a.max_pages);
   int32_t* list = reinterpret_cast<int32_t*>(dyn + 2 * round4(a.max_pages));
 
-  const int32_t* ptb = s.pt + (size_t)b * s.pt_stride;
-  for (int i = tid; i < n_b; i += NT) prow[i] = ptb[i];
-  if (scoring) head_query_mean<T, D, NT>(s, b, h, qbar);
+#pragma unroll
+  for (int j = 0; j < kSpec; ++j) {
+    const int i = tid + j * NT;
+    if (i < n_b) prow[i] = pv[j];
+  }
+  for (int i = tid + kSpec * NT; i < n_b; i += NT) prow[i] = ptb[i];
   select_init<NT>(sl);
   __syncthreads();
 
