@@ -76,39 +76,33 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   int32_t* phys = reinterpret_cast<int32_t*>(smem + a.H_kv * D);
 
   const int b = blockIdx.y;
-  int seq = a.seq_lens[b];
-  seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
-  const int n_b = (seq + a.S_p - 1) / a.S_p;
-  const int n_cand = n_b - a.n_bos - a.n_eos;
-  const int c0 = blockIdx.x * a.cand_per_block;
-  if (c0 >= n_cand) return;
-  const int c1 = min(c0 + a.cand_per_block, n_cand);
-  const int nc = c1 - c0;
   const int tid = threadIdx.x;
-
   // group-mean query of every KV head, fp32: thread (chunk, head, segment)
   // sums eight query heads in order, the chunks' partials are then added in
-  // chunk order (one round of loads for any G <= 8 * 512 / (H_kv * LH))
+  // chunk order.  The first item's query loads and the first page-table
+  // entry are issued before the request length is known.
   const int G = a.H_q / a.H_kv;
   const int NCH = (G + 7) / 8;
   const int QS = a.H_kv * LH;                 // (head, segment) pairs
   const T* qb = reinterpret_cast<const T*>(a.q) + (size_t)b * a.H_q * D;
   const float invG = 1.0f / (float)G;
   float* qpart = reinterpret_cast<float*>(phys + a.cand_per_block);   // [NCH][H_kv * D] when NCH > 1
-  for (int i = tid; i < QS * NCH; i += kScoreThreads) {
+  auto q_load = [&](int i, uint4* v) {
     const int ch = i / QS, hs = i - ch * QS;
     const int h = hs / LH, sg = hs - h * LH;
-    const int g0 = ch * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (ch * 8 + j < G) v[j] = ld16(qb + (size_t)(h * G + ch * 8 + j) * D + sg * E);
+  };
+  auto q_store = [&](int i, const uint4* v) {
+    const int ch = i / QS, hs = i - ch * QS;
+    const int h = hs / LH, sg = hs - h * LH;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    uint4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (g0 + j < G) v[j] = ld16(qb + (size_t)(h * G + g0 + j) * D + sg * E);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (g0 + j < G) {
+      if (ch * 8 + j < G) {
         float f[E];
         V::unpack(v[j], f);
 #pragma unroll
@@ -118,6 +112,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     float* dst = NCH == 1 ? qbar : qpart + (size_t)ch * a.H_kv * D;
 #pragma unroll
     for (int e = 0; e < E; ++e) dst[h * D + sg * E + e] = NCH == 1 ? acc[e] * invG : acc[e];
+  };
+  uint4 qv[8];
+  if (tid < QS * NCH) q_load(tid, qv);
+  const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
+  const int c0 = blockIdx.x * a.cand_per_block;
+  const int pv = tid < a.cand_per_block && c0 + tid < a.score_stride - a.n_bos ? ptb[c0 + tid] : 0;
+
+  int seq = a.seq_lens[b];
+  seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
+  const int n_b = (seq + a.S_p - 1) / a.S_p;
+  const int n_cand = n_b - a.n_bos - a.n_eos;
+  if (c0 >= n_cand) return;
+  const int c1 = min(c0 + a.cand_per_block, n_cand);
+  const int nc = c1 - c0;
+
+  if (tid < QS * NCH) q_store(tid, qv);
+  for (int i = tid + kScoreThreads; i < QS * NCH; i += kScoreThreads) {
+    q_load(i, qv);
+    q_store(i, qv);
   }
   if (NCH > 1) {
     __syncthreads();
@@ -127,8 +140,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       qbar[i] = x * invG;
     }
   }
-  const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
-  for (int i = tid; i < nc; i += kScoreThreads) phys[i] = ptb[c0 + i];
+  if (tid < nc) phys[tid] = pv;
+  for (int i = tid + kScoreThreads; i < nc; i += kScoreThreads) phys[i] = ptb[c0 + i];
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;
