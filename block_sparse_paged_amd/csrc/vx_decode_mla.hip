@@ -17,9 +17,8 @@
 //   - O += P V: wave w owns V dims 128w..128w+127 (2 head tiles x 8 dim tiles
 //     of 16x16 accumulators).  V is read from the K tile already in LDS, so
 //     HBM sees each 576-dim row once.  The MFMA contracts over tokens: lane
-//     group g takes tokens g, g+4, ..., g+28, with P stored in LDS in the same
-//     order and the LDS row stride padded to 296 dwords so the four groups hit
-//     disjoint banks.
+//     group g takes tokens 8g .. 8g+7, read two rows of four at a time with
+//     the transposing 64-bit LDS read; P is stored [head][token].
 #include "vx_device.h"
 #include "vx_internal.h"
 
@@ -27,6 +26,8 @@ namespace vx {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDqk = 576, kDv = 512, kHeads = 32;
@@ -169,8 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
       const float p = (m_new == neg_inf()) ? 0.f : exp2f(sv[i] - m_new);
       const bf16_t pb = f32_to_bf16(p);
       psum += Vec16<bf16_t>::to_f32(pb);
-      // token 16*tw + 4*lg + i  ->  g = i, slot = 4*tw + lg
-      ptile[head * kT + i * 8 + 4 * tw + lg] = pb;
+      ptile[head * kT + 16 * tw + 4 * lg + i] = pb;    // [head][token]
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
@@ -202,11 +202,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
           bf16x8, *reinterpret_cast<const uint4*>(ptile + (16 * ht + lr) * kT + 8 * lg));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int d = 128 * w + 16 * dt + lr;
-      bf16x8 vB;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vB[i] = *reinterpret_cast<const __bf16*>(ktile + (4 * i + lg) * kLdsRow + 2 * d);
+      // V rows 8lg .. 8lg+7, dims 128w + 16dt .. +15, transposed by the LDS
+      // read: lane 16g + i gets dim i of four rows supplied by lanes
+      // 16g + 4j + c (row 8g + j (+4), dims 4c .. 4c+3)
+      const uint8_t* vsrc = ktile + (8 * lg + (lr >> 2)) * kLdsRow + 2 * (128 * w + 16 * dt + 4 * (lr & 3));
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vsrc));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vsrc + 4 * kLdsRow));
+      const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      const bf16x8 vB = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
         f32x4 acc = o[ht][dt];
