@@ -6,19 +6,20 @@
 // exactly over them; this kernel is the attention half.
 //
 // At ~60 flop per byte of KV this is past the fp32 VALU roofline, so both
-// products run on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accum).
-// One 256-thread block per (split, request).  Per 32-token tile (36 KiB):
+// products run on gfx950 matrix cores (fp32 accumulation).  One 256-thread
+// block per (split, request); per 32-token tile (36 KiB), three barriers:
 //   - all threads copy the tile HBM -> registers -> LDS, the next tile's
 //     global loads being in flight while the current one is computed;
-//   - S^T = K Q^T: wave w owns tokens 16*(w&1).. and heads 16*(w>>1)..; the
-//     query stays in registers as the MFMA B operand (18 k-steps of 32 dims);
-//   - online softmax per head, the two token halves exchanging their maxima
-//     and sums through LDS; P goes to LDS in bf16;
-//   - O += P V: wave w owns V dims 128w..128w+127 (2 head tiles x 8 dim tiles
-//     of 16x16 accumulators).  V is read from the K tile already in LDS, so
-//     HBM sees each 576-dim row once.  The MFMA contracts over tokens: lane
-//     group g takes tokens 8g .. 8g+7, read two rows of four at a time with
-//     the transposing 64-bit LDS read; P is stored [head][token].
+//   - S^T[32 tokens x 32 heads] = K Q^T on mfma_f32_32x32x16_bf16, each wave
+//     over its own 144 of the 576 dims (its query slice stays in registers);
+//     the four partial products meet in LDS and every wave adds them in wave
+//     order, so each wave holds the whole S^T;
+//   - the online softmax of the 32 heads then needs no exchange: a lane holds
+//     16 tokens of one head, the other 16 sit in the lane 32 apart;
+//   - O^T[dims x heads] += V^T P^T on the same MFMA: wave w owns V dims
+//     128w .. 128w+127 (4 tiles of 32); P is already in the B operand layout
+//     in registers; V^T is read from the K tile in LDS (so HBM sees each
+//     576-dim row once) with the transposing 64-bit LDS read.
 #include "vx_device.h"
 #include "vx_internal.h"
 
@@ -28,35 +29,33 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDqk = 576, kDv = 512, kHeads = 32;
 constexpr int kPage = 64;                    // tokens per page
 constexpr int kT = 32;                       // tokens per tile
 constexpr int kRowB = kDqk * 2;              // 1152 bytes per token row
-constexpr int kLdsRow = kRowB + 32;          // padded LDS row stride (296 dwords)
+constexpr int kLdsRow = kRowB + 32;          // padded LDS row stride
 constexpr int kThreads = 256;
 constexpr int kChunksPerRow = kRowB / 16;    // 72
 constexpr int kLoads = kT * kChunksPerRow / kThreads;   // 9 x 16 B per thread per tile
+constexpr int kKS = kDqk / 4 / 16;           // 9 k-steps of 16 dims per wave
+constexpr int kPartStride = 20;              // floats per lane in the partial-S buffer (16 + pad)
 constexpr int kMaxPages = 256;               // pages per split (planner bound)
 static_assert(kT * kChunksPerRow == kLoads * kThreads, "tile copy");
+static_assert(kKS * 16 * 4 == kDqk, "k split");
 
 __device__ __forceinline__ float neg_inf() { return -INFINITY; }
 
 __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint8_t ktile[kT * kLdsRow];
-  __shared__ __align__(16) bf16_t ptile[kHeads * kT];   // [head][g][i] = P[head][4i+g]
-  __shared__ float red_max[2][kHeads];
-  __shared__ float red_sum[2][kHeads];
-  __shared__ float m_state[2][kHeads];
-  __shared__ float l_state[kHeads];
+  __shared__ __align__(16) float spart[4][64 * kPartStride];
   __shared__ int page_phys[kMaxPages];
   __shared__ int page_logi[kMaxPages];
   __shared__ int s_count;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int lg = l >> 4, lr = l & 15;          // lane group (k-block), row in group
-  const int tw = w & 1, hw = w >> 1;
+  const int hl = l & 31, hh = l >> 5;          // head (column) and k half of the 32x32 layouts
   const int split = blockIdx.x, b = blockIdx.y;
   const int G = a.H_q;                          // H_kv == 1
 
@@ -77,10 +76,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
     }
     if (l == 0) s_count = count;
   }
-  if (tid < kHeads) {
-    m_state[0][tid] = neg_inf();
-    l_state[tid] = 0.f;
-  }
   __syncthreads();
   const int count = s_count;
   const int p0 = split * a.pages_per_split;
@@ -93,23 +88,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
     page_phys[i] = ptb[logi];
   }
 
-  // query as the B operand of S^T = K Q^T: head 16*hw + lr, dims 32*ks + 8*lg ..
-  bf16x8 qB[kDqk / 32];
+  // query slice as the B operand of S^T = K Q^T: head hl, dims 144w + 16ks + 8hh ..
+  bf16x8 qB[kKS];
   {
-    const int head = 16 * hw + lr;
-    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.H_q + head) * kDqk;
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.H_q + hl) * kDqk;
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) {
-      uint4 v = head < G ? ld16(qp + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < kKS; ++ks) {
+      const uint4 v = hl < G ? ld16(qp + 144 * w + 16 * ks + 8 * hh) : make_uint4(0, 0, 0, 0);
       qB[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  f32x4 o[2][8];
+  // o[dt][i] = O[head hl][dim 128w + 32dt + 8(i/4) + 4hh + i%4]
+  f32x16 o[4];
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m = neg_inf(), lsum = 0.f;              // of head hl (the same in lanes hl and hl + 32)
 
   __syncthreads();                               // page lists visible
 
@@ -124,9 +120,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
   };
   if (n_tiles > 0) load_tile(0);
 
-  int par = 0;
+  // this lane's row / column in the transposing V reads: group g = l / 16 covers
+  // dims 16(g % 2) .. of a 32-dim tile and the token half hh; lane 16g + 4j + c
+  // supplies row 4hh + j (+8, +16 s) at dims 4c .. 4c+3
+  const int tr_row = 4 * hh + ((l & 15) >> 2);
+  const int tr_col = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+
   for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();                             // previous tile fully consumed
+    __syncthreads();                             // previous tile and partials consumed
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
       const int c = tid + r * kThreads;
@@ -139,119 +140,118 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
     const int j = t / (kPage / kT), half = t % (kPage / kT);
     const int tok0 = page_logi[j] * kPage + half * kT;
 
-    // ---- S^T tile: tokens 16*tw + 4*lg + i, head 16*hw + lr
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint8_t* krow = ktile + (16 * tw + lr) * kLdsRow + 16 * lg;
+    // ---- partial S^T over dims 144w .. 144w + 143
+    f32x16 sp;
 #pragma unroll
-      for (int ks = 0; ks < kDqk / 32; ++ks) {
-        const bf16x8 kA = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 64 * ks));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qB[ks], s, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) sp[i] = 0.f;
+    {
+      const uint8_t* krow = ktile + hl * kLdsRow + 2 * (144 * w + 8 * hh);
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8 kA = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 32 * ks));
+        sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA, qB[ks], sp, 0, 0, 0);
       }
     }
-    const int head = 16 * hw + lr;
-    float sv[4];
+    {
+      float* dst = spart[w] + l * kPartStride;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *reinterpret_cast<float4*>(dst + 4 * v) = make_float4(sp[4 * v], sp[4 * v + 1], sp[4 * v + 2], sp[4 * v + 3]);
+    }
+    __syncthreads();
+    // whole S^T in every wave: partials added in wave order
+    float sv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float* src = spart[v] + l * kPartStride;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = *reinterpret_cast<const float4*>(src + 4 * q4);
+        sv[4 * q4] += x.x;
+        sv[4 * q4 + 1] += x.y;
+        sv[4 * q4 + 2] += x.z;
+        sv[4 * q4 + 3] += x.w;
+      }
+    }
+    // ---- online softmax of head hl over the tile's tokens 8(i/4) + 4hh + i%4
     float mx = neg_inf();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pos = tok0 + 16 * tw + 4 * lg + i;
-      sv[i] = pos < seq ? s[i] * a.scale_log2 : neg_inf();
+    for (int i = 0; i < 16; ++i) {
+      const int pos = tok0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      sv[i] = pos < seq ? sv[i] * a.scale_log2 : neg_inf();
       mx = fmaxf(mx, sv[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (lg == 0) red_max[tw][head] = mx;
-    __syncthreads();
-    const float m_old = m_state[par][head];
-    const float m_new = fmaxf(m_old, fmaxf(red_max[0][head], red_max[1][head]));
-    float psum = 0.f;
+    {
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    }
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == neg_inf()) ? 1.f : exp2f(m - m_new);
+    m = m_new;
+    s16x8 pk[2];
+    float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
       const float p = (m_new == neg_inf()) ? 0.f : exp2f(sv[i] - m_new);
-      const bf16_t pb = f32_to_bf16(p);
-      psum += Vec16<bf16_t>::to_f32(pb);
-      ptile[head * kT + 16 * tw + 4 * lg + i] = pb;    // [head][token]
+      ps += p;
+      pk[i >> 3][i & 7] = (short)f32_to_bf16(p);
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    if (lg == 0) {
-      red_sum[tw][head] = psum;
-      if (tw == 0) m_state[par ^ 1][head] = m_new;
+    {
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps),
+                                                        false, false);
+      ps = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
     }
-    __syncthreads();
-    if (tid < kHeads) {
-      const float mo = m_state[par][tid], mn = m_state[par ^ 1][tid];
-      const float alpha = (mn == neg_inf()) ? 1.f : exp2f(mo - mn);
-      l_state[tid] = l_state[tid] * alpha + red_sum[0][tid] + red_sum[1][tid];
-    }
+    lsum = lsum * alpha + ps;
 
-    // ---- O += P V for dims 128*w .. 128*w + 127
-    float alpha[2][4];
+    // ---- O^T += V^T P^T over the tile's two 16-token slices
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x16 acc = o[dt];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 16 * ht + 4 * lg + i;
-        const float mo = m_state[par][h], mn = m_state[par ^ 1][h];
-        alpha[ht][i] = (mn == neg_inf()) ? 1.f : exp2f(mo - mn);
+      for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const uint8_t* vsrc = ktile + (16 * sl + tr_row) * kLdsRow + 2 * (128 * w + 32 * dt + tr_col);
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vsrc));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vsrc + 8 * kLdsRow));
+        const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                      __builtin_bit_cast(bf16x8, pk[sl]), acc, 0, 0, 0);
       }
-    bf16x8 pA[2];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-      pA[ht] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(ptile + (16 * ht + lr) * kT + 8 * lg));
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      // V rows 8lg .. 8lg+7, dims 128w + 16dt .. +15, transposed by the LDS
-      // read: lane 16g + i gets dim i of four rows supplied by lanes
-      // 16g + 4j + c (row 8g + j (+4), dims 4c .. 4c+3)
-      const uint8_t* vsrc = ktile + (8 * lg + (lr >> 2)) * kLdsRow + 2 * (128 * w + 16 * dt + 4 * (lr & 3));
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vsrc));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vsrc + 4 * kLdsRow));
-      const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      const bf16x8 vB = __builtin_bit_cast(bf16x8, vv);
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        f32x4 acc = o[ht][dt];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= alpha[ht][i];
-        o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pA[ht], vB, acc, 0, 0, 0);
-      }
+      o[dt] = acc;
     }
-    par ^= 1;
   }
-  __syncthreads();
 
-  // ---- write: o[ht][dt][i] is O[head 16*ht + 4*lg + i][dim 128*w + 16*dt + lr]
+  // ---- write: o[dt][i] is O[head hl][dim 128w + 32dt + 8(i/4) + 4hh + i%4]
+  if (hl >= G) return;
+  const size_t row = (size_t)b * a.H_q + hl;
   const bool direct = a.n_split == 1;
+  if (direct) {
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    bf16_t* op = reinterpret_cast<bf16_t*>(a.out) + row * kDv;
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * ht + 4 * lg + i;
-      if (h >= G) continue;
-      const float m = m_state[par][h], lt = l_state[h];
-      const size_t row = (size_t)b * a.H_q + h;
-      if (direct) {
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-        bf16_t* op = reinterpret_cast<bf16_t*>(a.out) + row * kDv;
+      for (int i = 0; i < 16; ++i)
+        op[128 * w + 32 * dt + 8 * (i >> 2) + 4 * hh + (i & 3)] = f32_to_bf16(o[dt][i] * inv);
+    if (w == 0 && hh == 0 && a.lse) a.lse[row] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : neg_inf();
+  } else {
+    const size_t prow = row * a.n_split + split;
+    float* po = a.part_o + prow * kDv;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) op[128 * w + 16 * dt + lr] = f32_to_bf16(o[ht][dt][i] * inv);
-        if (w == 0 && lr == 0 && a.lse)
-          a.lse[row] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : neg_inf();
-      } else {
-        const size_t prow = row * a.n_split + split;
-        float* po = a.part_o + prow * kDv;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) po[128 * w + 16 * dt + lr] = o[ht][dt][i];
-        if (w == 0 && lr == 0) {
-          a.part_ml[prow * 2] = m;
-          a.part_ml[prow * 2 + 1] = lt;
-        }
-      }
+      for (int i = 0; i < 16; ++i) po[128 * w + 32 * dt + 8 * (i >> 2) + 4 * hh + (i & 3)] = o[dt][i];
+    if (w == 0 && hh == 0) {
+      a.part_ml[prow * 2] = m;
+      a.part_ml[prow * 2 + 1] = lsum;
     }
+  }
 }
 
 }  // namespace
