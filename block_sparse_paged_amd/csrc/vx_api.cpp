@@ -157,14 +157,26 @@ size_t score_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt) {
 
 vx_status hip_status(hipError_t e) { return e == hipSuccess ? VX_OK : VX_ERR_HIP; }
 
+// Selection done inside the split decode kernel from the indexer's scores
+// (the fused step's fallback for few (request, KV head) units).
+struct SelectInDecode {
+  const float* scores;
+  int32_t* sel_out;
+  int32_t score_stride, topk, n_bos, n_eos;
+  size_t ws_offset;        // partials start here in the workspace (after the scores)
+};
+
 vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
                      const int32_t* sel, int32_t k_tot, float sm_scale, void* out, float* lse,
-                     void* ws, size_t ws_bytes, hipStream_t stream) {
-  const bool sparse = sel != nullptr;
+                     void* ws, size_t ws_bytes, hipStream_t stream,
+                     const SelectInDecode* fs = nullptr) {
+  const bool sparse = sel != nullptr || fs != nullptr;
   const DecodePlan p = plan_decode(kv, bt, sparse ? k_tot : max_pages_eff(kv, bt), sparse);
-  if (ws_bytes < p.ws_bytes()) return VX_ERR_WORKSPACE_TOO_SMALL;
+  const size_t off = fs ? fs->ws_offset : 0;
+  if (ws_bytes < off + p.ws_bytes()) return VX_ERR_WORKSPACE_TOO_SMALL;
   if (p.ws_bytes() > 0 && ws == nullptr) return VX_ERR_INVALID_ARGUMENT;
   if (bt->batch == 0) return VX_OK;
+  ws = reinterpret_cast<char*>(ws) + off;
 
   DecodeArgs a{};
   a.q = q;
@@ -186,6 +198,14 @@ vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.out = out;
   a.lse = lse;
+  if (fs) {
+    a.scores = fs->scores;
+    a.sel_out = fs->sel_out;
+    a.score_stride = fs->score_stride;
+    a.topk = fs->topk;
+    a.n_bos = fs->n_bos;
+    a.n_eos = fs->n_eos;
+  }
   if (p.n_split > 1) {
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_o_bytes);
@@ -208,6 +228,9 @@ vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
   }
   return hip_status(e);
 }
+
+hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                              int32_t n_bos, int32_t n_eos, float* scores, hipStream_t stream);
 
 vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                           int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
@@ -272,6 +295,18 @@ vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const vo
   }
 
   if (need_scores) {
+    hipError_t e = launch_split_score(kv, batch, q, n_bos, n_eos, scores, stream);
+    if (e != hipSuccess) return VX_ERR_HIP;
+  }
+  return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
+}
+
+// The split indexer's scoring kernel alone: fp32 scores [B, H_kv, mp] into `scores`.
+hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                              int32_t n_bos, int32_t n_eos, float* scores, hipStream_t stream) {
+  const int mp = max_pages_eff(kv, batch);
+  const int max_cand = std::max(mp - n_bos - n_eos, 0);
+  {
     ScoreArgs s{};
     s.q = q;
     s.cent = kv->centroids;
@@ -285,7 +320,7 @@ vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const vo
     s.S_p = kv->page_size;
     s.pt_stride = batch->max_pages_per_req;
     s.score_stride = mp;
-    s.max_tokens = max_tokens;
+    s.max_tokens = batch->max_seq_len;
     s.n_bos = n_bos;
     s.n_eos = n_eos;
     // about one 8-wave block per CU in all: each request's candidates are
@@ -294,24 +329,29 @@ vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const vo
     int cpb = ceil_div(max_cand, nblk);
     cpb = std::max(32, (cpb + 7) / 8 * 8);
     s.cand_per_block = cpb;
-    hipError_t e = launch_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
-    if (e != hipSuccess) return VX_ERR_HIP;
+    return launch_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
   }
-  return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
 }
 
 size_t step_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
-  return std::max(score_ws_bytes(kv, bt), plan_decode(kv, bt, k_tot, true).ws_bytes());
+  // the indexer's scores and the decode partials side by side (the decode
+  // kernel may select from the scores while it writes partials)
+  return align_up(score_ws_bytes(kv, bt)) + plan_decode(kv, bt, k_tot, true).ws_bytes();
 }
 
 // Dynamic LDS of the fused step kernel: staged page row and keys (one word
 // per page each) and the selected list; plus its static arrays.
-size_t step_lds_bytes(int max_pages, int k_tot, int D, int G, int ordered_batch) {
-  const size_t dyn = step_dynamic_lds(max_pages, k_tot, ordered_batch);
-  // attention: per-wave partials (VALU form) or per-wave V staging / partials (MFMA form)
+// LDS of an 8-wave attention block: per-wave partials (VALU form) or per-wave
+// V staging / partials (MFMA form), whichever is larger.
+size_t attention_lds_bytes(int D, int G) {
   const size_t att_valu = 8 * (size_t)G * (D + 2) * 4;
   const size_t att_mfma = 8 * std::max((size_t)16 * (2 * D + 32), (size_t)G * D * 4) + 2 * 8 * (size_t)G * 4;
-  const size_t stat = (size_t)D * 4 + kSelectLdsBytes + std::max(att_valu, att_mfma) +
+  return std::max(att_valu, att_mfma);
+}
+
+size_t step_lds_bytes(int max_pages, int k_tot, int D, int G, int ordered_batch) {
+  const size_t dyn = step_dynamic_lds(max_pages, k_tot, ordered_batch);
+  const size_t stat = (size_t)D * 4 + kSelectLdsBytes + attention_lds_bytes(D, G) +
                       16 * (size_t)D * 4 + 16;
   return dyn + stat;
 }
@@ -476,6 +516,23 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
     c.pt_stride = batch->max_pages_per_req;
     c.max_tokens = batch->max_seq_len;
     if (launch_centroid(kv->dtype, c, stream) != hipSuccess) return VX_ERR_HIP;
+  }
+  // The split scorer's scores are selected from inside the split decode
+  // kernel (no top-k launch) when its keys fit in LDS beside the attention.
+  const int max_cand = std::max(mp - n_bos - n_eos, 0);
+  const bool split_scorer = !(fused_indexer_supported(kv->dtype, kv->head_dim_qk) &&
+                              mp <= kFusedMaxPages &&
+                              (units >= kNumCUs / 2 || units * mp <= 4096));
+  const size_t sel_lds = (size_t)(round4(mp) + k_tot) * 4 + kSelectLdsBytes +
+                         attention_lds_bytes(kv->head_dim_qk, G);
+  if (!is_mla(kv) && split_scorer && max_cand > topk && topk > 0 &&
+      sel_lds <= max_lds_per_block()) {
+    float* scores = reinterpret_cast<float*>(workspace);
+    if (launch_split_score(kv, batch, q, n_bos, n_eos, scores, stream) != hipSuccess)
+      return VX_ERR_HIP;
+    SelectInDecode fs{scores, sel, mp, topk, n_bos, n_eos, align_up(score_ws_bytes(kv, batch))};
+    return run_decode(kv, batch, q, nullptr, k_tot, sm_scale, out, lse, workspace,
+                      workspace_bytes, stream, &fs);
   }
   st = score_topk_impl(kv, batch, q, topk, n_bos, n_eos, sel, workspace, workspace_bytes, stream);
   if (st != VX_OK) return st;

@@ -8,51 +8,104 @@
 // K4: one block of 8 waves per (split, KV head, request) runs attend_pages()
 // over its range of the page list.  A selection row of up to 64 pages is read
 // once, one entry per lane, and its page ids are shuffled to the waves that
-// need them; longer lists are read from memory per page.  The block writes
-// the output directly when the plan has a single split, else fp32 partials.
+// need them; longer lists are read from memory per page.  In the fused form
+// (indexer scores given) every split block selects its (request, KV head)'s
+// pages from the scores itself, with the exact selection of the indexer
+// kernels, instead of a separate top-k launch; split 0 writes the selection
+// row.  The block writes the output directly when the plan has a single
+// split, else fp32 partials.
 // K5: merges the partials of each (request, query head).
 #include "vx_attend.h"
+#include "vx_select.h"
 
 namespace vx {
 namespace {
 
-template <typename T, int D, int G, int HS, int PF>
-__global__ __launch_bounds__(kNW * 64) void decode_valu_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & 63;
+template <typename T, int D, int G, int HS, int PF, bool SELECT>
+__global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeArgs a) {
+  constexpr int NT = kNW * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   int seq = a.seq_lens[b];
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
-
-  // length of this request's page list (the selection ends at its first
-  // entry outside [0, n_b))
-  const int32_t* selrow = nullptr;
-  int count = n_b, sel_l = 0;
-  const bool sel_in_regs = a.sel && a.k_tot <= 64;
-  if (a.sel) {
-    selrow = a.sel + ((size_t)b * a.H_kv + h) * a.k_tot;
-    count = a.k_tot;
-    for (int base = 0; base < a.k_tot; base += 64) {
-      const int i = base + lane;
-      const int p = i < a.k_tot ? selrow[i] : 0;
-      if (base == 0) sel_l = p;
-      const unsigned long long bad = __ballot(i < a.k_tot && (p < 0 || p >= n_b));
-      if (bad) { count = base + __builtin_ctzll(bad); break; }
-    }
-  }
-  const int p0 = split * a.pages_per_split;
-  const int p1 = min(p0 + a.pages_per_split, count);
   const int32_t* ptb = a.pt + (size_t)b * a.pt_stride;
-  auto page_at = [&](int idx, bool active) -> int2 {
-    const int from_regs = __shfl(sel_l, idx & 63, 64);
-    int logi = idx, phys = 0;
-    if (active) {
-      if (selrow) logi = sel_in_regs ? from_regs : selrow[idx];
-      phys = ptb[logi];
+
+  if constexpr (SELECT) {
+    // the (request, KV head)'s selection, computed by every split block
+    extern __shared__ __align__(16) uint32_t dyn[];   // keys [round4(score_stride)], list [k_tot]
+    __shared__ SelectLds<NT> sl;
+    uint32_t* keys = dyn;
+    int32_t* list = reinterpret_cast<int32_t*>(dyn + round4(a.score_stride));
+    const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
+    select_init<NT>(sl);
+    __syncthreads();
+    if (n_cand > a.topk && a.topk > 0) {
+      const float* sc = a.scores + ((size_t)b * a.H_kv + h) * a.score_stride;
+      for (int i0 = tid; i0 < n_cand; i0 += 8 * NT) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = i0 + j * NT < n_cand ? sc[i0 + j * NT] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = i0 + j * NT;
+          if (i < n_cand) {
+            const uint32_t k = order_key(v[j]);
+            keys[i] = k;
+            select_count<NT>(sl, k);
+          }
+        }
+      }
     }
-    return make_int2(logi, phys);
-  };
-  attend_pages<T, D, G, HS, PF, kNW>(a, b, h, split, p0, p1, seq, page_at);
+    const int count = select_pages<NT>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
+                                       nullptr, list, sl);
+    __syncthreads();
+    const int p0 = split * a.pages_per_split;
+    const int p1 = min(p0 + a.pages_per_split, count);
+    auto page_at = [&](int idx, bool active) -> int2 {
+      int logi = 0, phys = 0;
+      if (active) {
+        logi = list[idx];
+        phys = ptb[logi];
+      }
+      return make_int2(logi, phys);
+    };
+    int32_t* srow = a.sel_out + ((size_t)b * a.H_kv + h) * a.k_tot;
+    auto epilogue = [&](int t, int nt) {
+      if (split == 0)
+        for (int i = t; i < a.k_tot; i += nt) srow[i] = i < count ? list[i] : -1;
+    };
+    attend_pages<T, D, G, HS, PF, kNW>(a, b, h, split, p0, p1, seq, page_at, epilogue);
+  } else {
+    // length of this request's page list (the selection ends at its first
+    // entry outside [0, n_b))
+    const int32_t* selrow = nullptr;
+    int count = n_b, sel_l = 0;
+    const bool sel_in_regs = a.sel && a.k_tot <= 64;
+    if (a.sel) {
+      selrow = a.sel + ((size_t)b * a.H_kv + h) * a.k_tot;
+      count = a.k_tot;
+      for (int base = 0; base < a.k_tot; base += 64) {
+        const int i = base + lane;
+        const int p = i < a.k_tot ? selrow[i] : 0;
+        if (base == 0) sel_l = p;
+        const unsigned long long bad = __ballot(i < a.k_tot && (p < 0 || p >= n_b));
+        if (bad) { count = base + __builtin_ctzll(bad); break; }
+      }
+    }
+    const int p0 = split * a.pages_per_split;
+    const int p1 = min(p0 + a.pages_per_split, count);
+    auto page_at = [&](int idx, bool active) -> int2 {
+      const int from_regs = __shfl(sel_l, idx & 63, 64);
+      int logi = idx, phys = 0;
+      if (active) {
+        if (selrow) logi = sel_in_regs ? from_regs : selrow[idx];
+        phys = ptb[logi];
+      }
+      return make_int2(logi, phys);
+    };
+    attend_pages<T, D, G, HS, PF, kNW>(a, b, h, split, p0, p1, seq, page_at);
+  }
 }
 
 // K5: merge the splits of one (request, query head).  Splits with an empty
@@ -129,7 +182,12 @@ template <typename T, int D, int G>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
   constexpr int HS = attend_head_slices<G>(), PF = attend_prefetch<T, D>();
   dim3 grid(a.n_split, a.H_kv, a.B);
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, G, HS, PF>), grid, dim3(kNW * 64), 0, s, a);
+  if (a.scores) {
+    const size_t lds = ((size_t)round4(a.score_stride) + (size_t)a.k_tot) * sizeof(uint32_t);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, HS, PF, true>), grid, dim3(kNW * 64), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, HS, PF, false>), grid, dim3(kNW * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

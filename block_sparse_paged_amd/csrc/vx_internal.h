@@ -56,6 +56,12 @@ struct DecodeArgs {
   int32_t pages_per_split, n_split;
   int32_t v_stride_tok;   // elements between consecutive tokens of V (D_qk when aliased)
   float scale_log2;       // sm_scale * log2(e)
+  // Selection in the decode kernel (scores != nullptr): every split block of
+  // a (request, KV head) selects its pages from the indexer's scores itself;
+  // split 0 writes the row of sel_out.
+  const float* scores;    // [B, H_kv, score_stride], candidate-indexed
+  int32_t* sel_out;       // [B, H_kv, k_tot]
+  int32_t score_stride, topk, n_bos, n_eos;
 };
 
 // One fused decode step per (request, KV head) block: completed-page
