@@ -22,7 +22,7 @@ namespace {
 using namespace vx;
 
 constexpr int kNumCUs = 256;                    // MI355X
-// blocks per launch the planner aims for (VALU decode blocks are 8 waves,
+// blocks per launch the planner aims for (split decode blocks are 8 waves,
 // MLA blocks 4): one wave of resident blocks for the sparse step, several
 // for the long dense stream so that unequal requests even out
 constexpr int kSparseTargetBlocks = kNumCUs;
@@ -212,7 +212,7 @@ vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
   }
   const int G = bt->num_q_heads / kv->num_kv_heads;
   hipError_t e = is_mla(kv) ? launch_decode_mla(a, stream)
-                            : launch_decode_valu(kv->dtype, kv->head_dim_qk, G, a, stream);
+                            : launch_decode_split(kv->dtype, kv->head_dim_qk, G, a, stream);
   if (e != hipSuccess) return VX_ERR_HIP;
   if (p.n_split > 1) {
     CombineArgs c{};

@@ -1,4 +1,4 @@
-// K4 (VALU) + K5: split-K paged decode attention over a list of logical
+// K4 + K5: split-K paged decode attention over a list of logical
 // pages (the selected ones, or every page for the dense baseline).  The
 // attention itself is the exact softmax attention the method runs after page
 // selection (Vortex article, "A dual-stage programmable abstraction"); the
@@ -210,7 +210,7 @@ hipError_t run_combine(const CombineArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode_valu(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_split(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s) {
   if (dtype == 0) {
     if (D == 64) return run_decode_g<float, 64>(G, a, s);
     if (D == 128) return run_decode_g<float, 128>(G, a, s);

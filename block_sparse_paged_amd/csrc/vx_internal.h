@@ -95,7 +95,7 @@ hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s);
 bool fused_indexer_supported(int dtype, int D);
 hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s);
 // D = D_qk = D_v for this path; G = H_q / H_kv.
-hipError_t launch_decode_valu(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_split(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 int mla_max_pages_per_split();
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
