@@ -353,7 +353,8 @@ def test_decode_step_incremental_hetero(vx):
 
 @pytest.mark.parametrize("topk,bos,eos", [(4, 1, 1), (0, 1, 1), (3, 0, 2)])
 @pytest.mark.parametrize("dtype,D,G,S", [("f32", 64, 1, 16), ("bf16", 128, 8, 16),
-                                         ("bf16", 128, 2, 64)])
+                                         ("bf16", 128, 2, 64), ("bf16", 64, 4, 16),
+                                         ("f32", 128, 4, 16), ("bf16", 128, 8, 64)])
 def test_decode_step_edge_lengths(vx, dtype, D, G, S, topk, bos, eos):
     lens = (1, S - 1, S, S + 1, S * 6, S * 6 + 1, S * 9 + 3)
     w = synth.Workload(name="edges", batch=len(lens), num_q_heads=2 * G, num_kv_heads=2,
@@ -496,3 +497,27 @@ def test_selection_refines_crowded_bin(vx):
     for b in range(w.batch):
         _check_request(vx, c, b, sel, out, lse)
         _check_request(vx, c, b, sel2, out2, lse2)
+
+
+@pytest.mark.parametrize("dtype,D,G", [("f32", 64, 2), ("bf16", 64, 4), ("f32", 128, 1)])
+def test_decode_step_few_units_long_rows(vx, dtype, D, G):
+    """Few (request, KV head) units with long page rows: the step scores with
+    the split indexer and every split block of the decode selects its pages
+    from those scores itself.  The selection equals vx_score_topk's and the
+    oracle's; outputs match the oracle."""
+    lens = (16 * 1500 + 9, 16 * 700)
+    w = synth.Workload(name="few_units", batch=len(lens), num_q_heads=2 * G, num_kv_heads=2,
+                       head_dim_qk=D, head_dim_v=D, page_size=16, dtype=dtype, topk=40,
+                       structure="page_offset", seed=82, seq_lens=lens, spare_pages=2)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    H.fix_gaps(c, range(w.batch))
+    q = c.q_host.cuda()
+    sel, out, lse = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, H.run_indexer(vx, c, q))
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel, out, lse)
+    H.assert_centroids(c, np.concatenate([synth.setup_full_pages(c.layout),
+                                          synth.completed_pages(c.layout, 0)]))
