@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeArgs a) {
       for (int i0 = tid; i0 < n_cand; i0 += 8 * NT) {
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = i0 + j * NT < n_cand ? sc[i0 + j * NT] : 0.f;
+        for (int j = 0; j < 8; ++j) v[j] = sc[min(i0 + j * NT, n_cand - 1)];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = i0 + j * NT;

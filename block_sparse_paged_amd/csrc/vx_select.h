@@ -42,7 +42,7 @@ template <int NT>
 struct SelectLds {
   alignas(16) int hist[2][kSelHistWords];
   int wsum[2][NT / 64];
-  int misc[4];
+  int misc[4];     // [0] tie threshold, [2] score_head's batch counter
 };
 
 static_assert(sizeof(SelectLds<512>) <= kSelectLdsBytes, "selection LDS bound");
@@ -53,6 +53,7 @@ template <int NT>
 __device__ __forceinline__ void select_init(SelectLds<NT>& S) {
   int* h = &S.hist[0][0];
   for (int i = threadIdx.x; i < 2 * kSelHistWords; i += NT) h[i] = 0;
+  if (threadIdx.x == 0) S.misc[2] = 0;
 }
 
 // Level-0 count of one key (any thread, any time before select_pages).
@@ -253,9 +254,19 @@ __device__ __forceinline__ void head_query_mean(const ScoreArgs& a, int b, int h
 // Scores of candidates [0, n_cand) of KV head h into LDS `keys` as
 // order-preserving keys, each counted into the selection's level-0
 // histogram; phys[c] is candidate c's physical page.  Rows are one head's
-// centroid row (<= 64 lanes of 16 bytes); each wave keeps kScoreLoads
-// wave-loads in flight.
+// centroid row (<= 64 lanes of 16 bytes).  A wave takes batches of U
+// wave-loads: each lane group reads U consecutive candidates' page ids from
+// LDS at once, then issues all of its row loads (past the last candidate the
+// index is clamped to it, so every load is unconditional and the rows are
+// consumed as they arrive).  Waves start on batches 0 .. NW-1 and then take
+// the next untaken batch, so that a wave whose loads return late does not
+// hold up the end of the scoring (keys and counts do not depend on which
+// wave computes them).  An 8-wave block has its CU alone and keeps 16
+// loads per wave in flight.  Blocks of fewer waves share a CU with a block
+// whose attention is a latency-bound chain of loads, and deeper queues slow
+// that chain more than they speed the scoring: they keep 6.
 constexpr int kScoreLoads = 16;
+constexpr int kScoreLoadsShared = 6;
 
 template <typename T, int D, int NT>
 __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand,
@@ -266,26 +277,32 @@ __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand
   constexpr int LH = D / E;                  // lanes per centroid row
   constexpr int R = 64 / LH;                 // rows per wave-load
   constexpr int NW = NT / 64;
-  constexpr int U = kScoreLoads;
+  constexpr int U = NW >= 8 ? kScoreLoads : kScoreLoadsShared;
+  constexpr int ROWS = R * U;                // rows per wave batch
   static_assert(LH * R == 64, "rows of at most 64 lanes");
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int seg = lane % LH, grp = lane / LH;
   float qr[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) qr[e] = qbar[seg * E + e];
-  const T* cent = reinterpret_cast<const T*>(a.cent);
-  constexpr int STEP = NW * R;               // rows per block-wide wave-load
-  for (int r0 = w * R; r0 < n_cand; r0 += STEP * U) {
+  const T* cent = reinterpret_cast<const T*>(a.cent) + (size_t)h * D + seg * E;
+  const size_t pstride = (size_t)a.H_kv * D;
+  const int last = n_cand - 1;
+  for (int bi = w;;) {                       // batch bi: candidates [bi * ROWS, +ROWS)
+    const int r0 = bi * ROWS;
+    if (r0 >= n_cand) break;
+    int next = 0;                            // the wave's next batch, taken from a counter
+    if (lane == 0) next = atomicAdd(&S.misc[2], 1);
+    const int c0 = r0 + grp * U;             // this lane group's first candidate
+    int ph[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ph[u] = phys[min(c0 + u, last)];
     uint4 buf[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = r0 + u * STEP + grp;
-      buf[u] = c < n_cand ? ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + seg * E)
-                          : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < U; ++u) buf[u] = ld16(cent + (size_t)ph[u] * pstride);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = r0 + u * STEP + grp;
+      const int c = c0 + u;
       float f[E];
       V::unpack(buf[u], f);
       float acc = 0.f;
@@ -298,6 +315,7 @@ __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand
         select_count<NT>(S, k);
       }
     }
+    bi = NW + __builtin_amdgcn_readfirstlane(next);
   }
 }
 
