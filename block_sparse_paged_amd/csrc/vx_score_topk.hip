@@ -162,21 +162,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) qr[e] = qbar[h0 * D + seg * E + e];
     }
-    // Page ids are read from LDS for the whole batch, then all of its row
-    // loads are issued (the row index is clamped to the last row, so no load
-    // is conditional and rows are used as they arrive).
-    const int last = rows - 1;
     for (int r0 = wave * R; r0 < rows; r0 += STEP * U) {
-      int row_at[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = min(r0 + u * STEP + grp, last);
-        const int c = r / a.H_kv, h = r - c * a.H_kv;
-        row_at[u] = phys[c] * a.H_kv + h;
-      }
       uint4 buf[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) buf[u] = ld16(cent + (size_t)row_at[u] * D + seg * E);
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * STEP + grp;
+        if (r < rows) {
+          const int c = r / a.H_kv, h = r - c * a.H_kv;
+          buf[u] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + seg * E);
+        } else {
+          buf[u] = make_uint4(0, 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int r = r0 + u * STEP + grp;
@@ -205,21 +202,24 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     constexpr int TL = LH - 64;             // tail segments per row (8)
     constexpr int RT = 64 / TL;             // rows per tile (8)
     struct Tile { uint4 hb[RT]; uint4 tb; };
-    auto issue = [&](int r0, Tile& tl) {   // rows past the last are clamped to it
-      const int last = rows - 1;
-      int row_at[RT];
+    auto issue = [&](int r0, Tile& tl) {
 #pragma unroll
       for (int i = 0; i < RT; ++i) {
-        const int r = min(r0 + i, last);
-        const int c = r / a.H_kv, h = r - c * a.H_kv;
-        row_at[i] = phys[c] * a.H_kv + h;
+        const int r = r0 + i;
+        if (r < rows) {
+          const int c = r / a.H_kv, h = r - c * a.H_kv;
+          tl.hb[i] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + lane * E);
+        } else {
+          tl.hb[i] = make_uint4(0, 0, 0, 0);
+        }
       }
-      const int tr = min(r0 + lane / TL, last), tseg = 64 + lane % TL;
-      const int tc = tr / a.H_kv, th = tr - tc * a.H_kv;
-      const int trow = phys[tc] * a.H_kv + th;
-#pragma unroll
-      for (int i = 0; i < RT; ++i) tl.hb[i] = ld16(cent + (size_t)row_at[i] * D + lane * E);
-      tl.tb = ld16(cent + (size_t)trow * D + tseg * E);
+      const int tr = r0 + lane / TL, tseg = 64 + lane % TL;
+      if (tr < rows) {
+        const int c = tr / a.H_kv, h = tr - c * a.H_kv;
+        tl.tb = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + tseg * E);
+      } else {
+        tl.tb = make_uint4(0, 0, 0, 0);
+      }
     };
     // with one KV head (MLA) the query segments a lane needs stay in registers
     const bool one_head = a.H_kv == 1;
@@ -293,7 +293,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     for (int i0 = tid; i0 < n_cand; i0 += 8 * kTopkThreads) {
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = sc[min(i0 + j * kTopkThreads, n_cand - 1)];
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + j * kTopkThreads;
+        v[j] = i < n_cand ? sc[i] : 0.f;
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = i0 + j * kTopkThreads;

@@ -37,6 +37,9 @@ constexpr int kSelShift0 = 32 - kSelBits;     // level-0 bin of a key: key >> 22
 __device__ __forceinline__ int sel_slot(int i) { return i + (i >> 4) * 4; }
 constexpr int kSelHistWords = kSelBins + kSelBins / 4;
 
+// 16-byte chunks of keys a thread keeps in registers during a selection.
+constexpr int kSelRegChunks = 4;
+
 // LDS of one selection (NT threads): two histograms (levels alternate).
 template <int NT>
 struct SelectLds {
@@ -123,6 +126,21 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
                                             int n_bos, int n_eos, int k_tot, int32_t* out,
                                             int32_t* lds_out, SelectLds<NT>& S) {
   const int tid = threadIdx.x;
+  // Thread tid owns candidates [c0, c0 + 4 nch), nch a power of two, as nch
+  // 16-byte chunks of keys.  Lanes 4a .. 4a+3 take their chunks starting at
+  // chunk a mod nch, so that a wave's 16-byte reads spread over all LDS
+  // banks.  Up to kSelRegChunks chunks are read once into registers and
+  // serve every refinement pass and the compaction.
+  int nch = 1;
+  while (4 * nch * NT < n_cand) nch <<= 1;
+  const int c0 = tid * 4 * nch;
+  const int rot = ((tid & 63) >> 2) & (nch - 1);
+  const bool in_regs = nch <= kSelRegChunks;
+  uint4 kr[kSelRegChunks];
+#pragma unroll
+  for (int jj = 0; jj < kSelRegChunks; ++jj) kr[jj] = make_uint4(0u, 0u, 0u, 0u);
+  auto reg_chunk = [&](int jj) { return c0 + 4 * ((jj + rot) & (nch - 1)); };
+
   // candidate c is taken iff keys[c] > thr_key || (keys[c] == thr_key && c <= thr_idx)
   uint32_t thr_key = 0u;
   int thr_idx = INT_MAX;                                  // all candidates
@@ -130,6 +148,14 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
     thr_key = 0xFFFFFFFFu;                                // none of them
     thr_idx = -1;
   } else if (n_cand > topk) {
+    __syncthreads();                   // keys and level-0 counts complete
+    if (in_regs) {
+#pragma unroll
+      for (int jj = 0; jj < kSelRegChunks; ++jj) {
+        const int c = reg_chunk(jj);
+        if (jj < nch && c < n_cand) kr[jj] = *reinterpret_cast<const uint4*>(keys + c);
+      }
+    }
     int remaining = topk;              // still to take from keys in [lo, lo + span]
     uint32_t lo = 0u, span = 0xFFFFFFFFu;
     int shift = kSelShift0;
@@ -140,17 +166,31 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
           for (int i = tid; i < kSelHistWords; i += NT) H[i] = 0;
           __syncthreads();
         }
-        for (int i0 = tid; i0 < n_cand; i0 += 4 * NT) {
-          uint32_t k[4];
+        auto count = [&](uint32_t k, int c) {
+          if (c < n_cand && k - lo <= span) atomicAdd(&H[sel_slot((int)((k - lo) >> shift))], 1);
+        };
+        if (in_regs) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) k[j] = i0 + j * NT < n_cand ? keys[i0 + j * NT] : 0u;
+          for (int jj = 0; jj < kSelRegChunks; ++jj) {
+            if (jj < nch) {
+              const int c = reg_chunk(jj);
+              count(kr[jj].x, c);
+              count(kr[jj].y, c + 1);
+              count(kr[jj].z, c + 2);
+              count(kr[jj].w, c + 3);
+            }
+          }
+        } else {
+          for (int i0 = tid; i0 < n_cand; i0 += 4 * NT) {
+            uint32_t k[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (i0 + j * NT < n_cand && k[j] - lo <= span)
-              atomicAdd(&H[sel_slot((int)((k[j] - lo) >> shift))], 1);
+            for (int j = 0; j < 4; ++j) k[j] = keys[min(i0 + j * NT, n_cand - 1)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) count(k[j], i0 + j * NT);
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
       int dsel, above, cnt;
       find_bin(H, remaining, dsel, above, cnt);
       remaining -= above;
@@ -162,13 +202,13 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
       }
       if (span == 0) {                 // cnt equal keys: the remaining-th in page order
         const int per = (n_cand + NT - 1) / NT;
-        const int c0 = min(tid * per, n_cand), c1 = min(c0 + per, n_cand);
+        const int e0 = min(tid * per, n_cand), e1 = min(e0 + per, n_cand);
         int n_eq = 0;
-        for (int i = c0; i < c1; ++i) n_eq += keys[i] == lo ? 1 : 0;
+        for (int i = e0; i < e1; ++i) n_eq += keys[i] == lo ? 1 : 0;
         int dummy;
         int r = block_exclusive_scan<NT>(n_eq, S.wsum[0], &dummy);
         if (r < remaining && r + n_eq >= remaining) {
-          for (int i = c0; i < c1; ++i)
+          for (int i = e0; i < e1; ++i)
             if (keys[i] == lo && ++r == remaining) S.misc[0] = i;
         }
         __syncthreads();
@@ -182,37 +222,64 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
   }
 
   // Compaction in page order: reserved first pages, taken candidates, reserved
-  // last pages.  Thread tid owns candidates [tid * per, tid * per + per),
-  // per a multiple of 4 (16-byte key reads).
-  int per = (n_cand + NT - 1) / NT;
-  per = (per + 3) & ~3;
-  const int c0 = tid * per;
+  // last pages.  Each thread's taken candidates become a bit mask (runs of
+  // up to 64 candidates when the keys are not in registers: those runs are
+  // read again to write them), then one block-wide scan places them.
+  auto taken = [&](uint32_t k, int c) {
+    return c < n_cand && (k > thr_key || (k == thr_key && c <= thr_idx));
+  };
+  const int per = 4 * nch;
+  const int run = min(nch, 16);                 // chunks per run
+  auto take_mask = [&](int s0) -> unsigned long long {   // from LDS: candidates c0 + s0 .. + 4 run
+    const int rr = ((tid & 63) >> 2) & (run - 1);
+    unsigned long long m = 0ull;
+    for (int jj = 0; jj < run; ++jj) {
+      const int j = (jj + rr) & (run - 1);
+      const int c = c0 + s0 + 4 * j;
+      if (c < n_cand) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(keys + c);
+        m |= (unsigned long long)(taken(kv.x, c) | taken(kv.y, c + 1) << 1 |
+                                  taken(kv.z, c + 2) << 2 | taken(kv.w, c + 3) << 3) << (4 * j);
+      }
+    }
+    return m;
+  };
+  unsigned long long m0 = 0ull;
   int n_take = 0;
-  for (int c = c0; c < c0 + per && c < n_cand; c += 4) {
-    const uint4 kv = *reinterpret_cast<const uint4*>(keys + c);
-    const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+  if (in_regs) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      n_take += (c + e < n_cand && (k4[e] > thr_key || (k4[e] == thr_key && c + e <= thr_idx)))
-                    ? 1 : 0;
+    for (int jj = 0; jj < kSelRegChunks; ++jj) {
+      if (jj < nch) {
+        const int c = reg_chunk(jj);
+        const unsigned t = taken(kr[jj].x, c) | taken(kr[jj].y, c + 1) << 1 |
+                           taken(kr[jj].z, c + 2) << 2 | taken(kr[jj].w, c + 3) << 3;
+        m0 |= (unsigned long long)t << (c - c0);
+      }
+    }
+    n_take = __popcll(m0);
+  } else {
+    for (int s0 = 0; s0 < per && c0 + s0 < n_cand; s0 += 4 * run) {
+      const unsigned long long m = take_mask(s0);
+      if (s0 == 0) m0 = m;
+      n_take += __popcll(m);
+    }
   }
-  int taken;
-  int pos = block_exclusive_scan<NT>(n_take, S.wsum[1], &taken);
+  int taken_all;
+  int pos = block_exclusive_scan<NT>(n_take, S.wsum[1], &taken_all);
   const int n_lo = n_cand > 0 ? n_bos : n_b;           // no candidates: every page is reserved
   const int n_hi = n_cand > 0 ? n_eos : 0;
-  const int total = n_lo + taken + n_hi;
+  const int total = n_lo + taken_all + n_hi;
   int32_t* dst = lds_out ? lds_out : out;
   pos += n_lo;
-  for (int c = c0; c < c0 + per && c < n_cand; c += 4) {
-    const uint4 kv = *reinterpret_cast<const uint4*>(keys + c);
-    const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (c + e < n_cand && (k4[e] > thr_key || (k4[e] == thr_key && c + e <= thr_idx)))
-        dst[pos++] = n_bos + c + e;
+  for (int s0 = 0; s0 < per && c0 + s0 < n_cand; s0 += 4 * run) {
+    unsigned long long m = s0 == 0 ? m0 : take_mask(s0);
+    while (m) {
+      dst[pos++] = n_bos + c0 + s0 + __builtin_ctzll(m);
+      m &= m - 1;
+    }
   }
   for (int i = tid; i < n_lo; i += NT) dst[i] = i;
-  for (int i = tid; i < n_hi; i += NT) dst[n_lo + taken + i] = n_b - n_eos + i;
+  for (int i = tid; i < n_hi; i += NT) dst[n_lo + taken_all + i] = n_b - n_eos + i;
   if (!lds_out)
     for (int i = total + tid; i < k_tot; i += NT) out[i] = -1;
   return total;
