@@ -230,11 +230,18 @@ vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
 }
 
 hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
-                              int32_t n_bos, int32_t n_eos, float* scores, hipStream_t stream);
+                              int32_t n_bos, int32_t n_eos, float* scores, bool update_completed,
+                              hipStream_t stream);
+hipError_t launch_completed_centroids(const vx_paged_kv* kv, const vx_batch* batch,
+                                      hipStream_t stream);
 
+// The indexer.  With update_completed (the decode step) it also writes the
+// centroids of the pages the batch's latest tokens completed: inside the
+// split scorer when that runs, else with the centroid kernel first.
 vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                           int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          bool update_completed = false) {
   vx_status st = check_kv(kv);
   if (st != VX_OK) return st;
   if ((st = check_batch(kv, batch)) != VX_OK) return st;
@@ -291,19 +298,45 @@ vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const vo
     s.n_bos = n_bos;
     s.n_eos = n_eos;
     s.scores = scores;     // not read by the fused kernel
+    if (update_completed && launch_completed_centroids(kv, batch, stream) != hipSuccess)
+      return VX_ERR_HIP;
     return hip_status(launch_indexer_fused(kv->dtype, s, t, stream));
   }
 
   if (need_scores) {
-    hipError_t e = launch_split_score(kv, batch, q, n_bos, n_eos, scores, stream);
+    hipError_t e = launch_split_score(kv, batch, q, n_bos, n_eos, scores, update_completed, stream);
     if (e != hipSuccess) return VX_ERR_HIP;
+  } else if (update_completed && launch_completed_centroids(kv, batch, stream) != hipSuccess) {
+    return VX_ERR_HIP;
   }
   return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
 }
 
-// The split indexer's scoring kernel alone: fp32 scores [B, H_kv, mp] into `scores`.
+// The centroid kernel over the page each request's latest token completed.
+hipError_t launch_completed_centroids(const vx_paged_kv* kv, const vx_batch* batch,
+                                      hipStream_t stream) {
+  CentroidArgs c{};
+  c.k = kv->k_cache;
+  c.cent = kv->centroids;
+  c.ids = nullptr;
+  c.pt = batch->page_table;
+  c.seq_lens = batch->seq_lens;
+  c.n_ids = batch->batch;
+  c.H_kv = kv->num_kv_heads;
+  c.S_p = kv->page_size;
+  c.D = kv->head_dim_qk;
+  c.pt_stride = batch->max_pages_per_req;
+  c.max_tokens = batch->max_seq_len;
+  return launch_centroid(kv->dtype, c, stream);
+}
+
+// The split indexer's scoring kernel alone: fp32 scores [B, H_kv, mp] into
+// `scores`.  With update_completed it also writes the completed pages'
+// centroids (in the kernel when it has a block for every KV head, else with
+// the centroid kernel first).
 hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
-                              int32_t n_bos, int32_t n_eos, float* scores, hipStream_t stream) {
+                              int32_t n_bos, int32_t n_eos, float* scores, bool update_completed,
+                              hipStream_t stream) {
   const int mp = max_pages_eff(kv, batch);
   const int max_cand = std::max(mp - n_bos - n_eos, 0);
   {
@@ -329,7 +362,18 @@ hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, cons
     int cpb = ceil_div(max_cand, nblk);
     cpb = std::max(32, (cpb + 7) / 8 * 8);
     s.cand_per_block = cpb;
-    return launch_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
+    const int grid_x = ceil_div(max_cand, cpb);
+    if (update_completed) {
+      if (grid_x >= kv->num_kv_heads && kv->page_size <= kMaxTileRows) {
+        s.k = kv->k_cache;
+        s.cent_out = kv->centroids;
+        s.update_completed = 1;
+      } else {
+        const hipError_t e = launch_completed_centroids(kv, batch, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+    return launch_score(kv->dtype, s, grid_x, stream);
   }
 }
 
@@ -501,22 +545,8 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
     return hip_status(launch_decode_step(kv->dtype, kv->head_dim_qk, G, waves, a, stream));
   }
 
-  // Otherwise: completed-page centroids, the indexer, then attention.
-  if (update_completed) {
-    CentroidArgs c{};
-    c.k = kv->k_cache;
-    c.cent = kv->centroids;
-    c.ids = nullptr;
-    c.pt = batch->page_table;
-    c.seq_lens = batch->seq_lens;
-    c.n_ids = batch->batch;
-    c.H_kv = kv->num_kv_heads;
-    c.S_p = kv->page_size;
-    c.D = kv->head_dim_qk;
-    c.pt_stride = batch->max_pages_per_req;
-    c.max_tokens = batch->max_seq_len;
-    if (launch_centroid(kv->dtype, c, stream) != hipSuccess) return VX_ERR_HIP;
-  }
+  // Otherwise: the indexer (with the completed pages' centroids), then
+  // attention.
   // The split scorer's scores are selected from inside the split decode
   // kernel (no top-k launch) when its keys fit in LDS beside the attention.
   const int max_cand = std::max(mp - n_bos - n_eos, 0);
@@ -528,13 +558,15 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
   if (!is_mla(kv) && split_scorer && max_cand > topk && topk > 0 &&
       sel_lds <= max_lds_per_block()) {
     float* scores = reinterpret_cast<float*>(workspace);
-    if (launch_split_score(kv, batch, q, n_bos, n_eos, scores, stream) != hipSuccess)
+    if (launch_split_score(kv, batch, q, n_bos, n_eos, scores, update_completed != 0, stream) !=
+        hipSuccess)
       return VX_ERR_HIP;
     SelectInDecode fs{scores, sel, mp, topk, n_bos, n_eos, align_up(score_ws_bytes(kv, batch))};
     return run_decode(kv, batch, q, nullptr, k_tot, sm_scale, out, lse, workspace,
                       workspace_bytes, stream, &fs);
   }
-  st = score_topk_impl(kv, batch, q, topk, n_bos, n_eos, sel, workspace, workspace_bytes, stream);
+  st = score_topk_impl(kv, batch, q, topk, n_bos, n_eos, sel, workspace, workspace_bytes, stream,
+                       update_completed != 0);
   if (st != VX_OK) return st;
   return run_decode(kv, batch, q, sel, k_tot, sm_scale, out, lse, workspace, workspace_bytes,
                     stream);

@@ -6,6 +6,7 @@
 #pragma once
 
 #include "vx_device.h"
+#include "vx_internal.h"
 
 namespace vx {
 
@@ -43,5 +44,67 @@ __device__ __forceinline__ uint4 centroid_segment(const T* tile, int S_p, int se
   for (int e = 0; e < E; ++e) sum[e] *= inv;
   return V::pack(sum);
 }
+
+// The centroid of one page-head tile computed inside a longer kernel of NT
+// threads, in the order of the centroid kernel: load() issues each thread's
+// rows early (thread t takes (row group, segment) pairs t, t + NT, ...),
+// reduce() sums them per row group into LDS `red` [RG][D] later, and after a
+// barrier finish() adds the groups in order for segment t < SEGS, scales and
+// stores.  Pages of up to kMaxTileRows rows.
+
+template <typename T, int D, int NT>
+struct TileCentroid {
+  using S = CentroidShape<T, D>;
+  static constexpr int CP = (S::THREADS + NT - 1) / NT;               // pairs per thread
+  static constexpr int CR = (kMaxTileRows + S::RG - 1) / S::RG;       // rows per pair
+  uint4 rows[CP][CR];
+
+  __device__ __forceinline__ void load(const T* tile, int S_p) {
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      const int pr = threadIdx.x + c * NT, g = pr / S::SEGS, sg = pr % S::SEGS;
+#pragma unroll
+      for (int j = 0; j < CR; ++j)
+        if (pr < S::THREADS && g + j * S::RG < S_p)
+          rows[c][j] = ld16(tile + (size_t)(g + j * S::RG) * D + sg * S::E);
+    }
+  }
+
+  __device__ __forceinline__ void reduce(float* red, int S_p) const {
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      const int pr = threadIdx.x + c * NT, g = pr / S::SEGS, sg = pr % S::SEGS;
+      if (pr < S::THREADS) {
+        float part[S::E];
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) part[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < CR; ++j) {
+          if (g + j * S::RG < S_p) {
+            float f[S::E];
+            Vec16<T>::unpack(rows[c][j], f);
+#pragma unroll
+            for (int e = 0; e < S::E; ++e) part[e] += f[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) red[g * D + sg * S::E + e] = part[e];
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void finish(const float* red, int S_p, T* cent_row, int t) {
+    float sum[S::E];
+#pragma unroll
+    for (int e = 0; e < S::E; ++e) sum[e] = 0.f;
+    for (int g = 0; g < S::RG; ++g)
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) sum[e] += red[g * D + t * S::E + e];
+    const float inv = 1.0f / (float)S_p;
+#pragma unroll
+    for (int e = 0; e < S::E; ++e) sum[e] *= inv;
+    st16(cent_row + t * S::E, Vec16<T>::pack(sum));
+  }
+};
 
 }  // namespace vx

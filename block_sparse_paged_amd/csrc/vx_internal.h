@@ -22,6 +22,9 @@ struct CentroidArgs {
   int32_t pt_stride, max_tokens;
 };
 
+// Most rows of a page-head tile whose centroid a longer kernel computes.
+constexpr int kMaxTileRows = 64;
+
 struct ScoreArgs {
   const void* q;          // [B, H_q, D]
   const void* cent;       // [P, H_kv, D]
@@ -31,6 +34,12 @@ struct ScoreArgs {
   int32_t B, H_q, H_kv, D, S_p, pt_stride, score_stride, max_tokens;
   int32_t n_bos, n_eos;
   int32_t cand_per_block;
+  // split scorer only: when set, blocks x < H_kv also write the centroid of
+  // KV head x of the page each request's latest token completed (that page
+  // is reserved, never a candidate)
+  const void* k;          // [P, H_kv, S_p, D]
+  void* cent_out;         // the centroid table, written
+  int32_t update_completed;
 };
 
 struct TopkArgs {

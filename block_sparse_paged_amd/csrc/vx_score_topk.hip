@@ -24,6 +24,7 @@
 // boundary bin itself), the boundary bin's keys ranked exactly (or the bin
 // histogrammed again when it holds more than 256), then the union with the
 // reserved pages compacted in ascending page order with one block-wide scan.
+#include "vx_centroid.h"
 #include "vx_select.h"
 
 namespace vx {
@@ -123,7 +124,30 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
   const int n_cand = n_b - a.n_bos - a.n_eos;
-  if (c0 >= n_cand) return;
+  // the completed page's centroid (blocks x < H_kv, head x): rows loaded now,
+  // summed after the scoring
+  using TC = TileCentroid<T, D, kScoreThreads>;
+  const bool upd = a.update_completed && (int)blockIdx.x < a.H_kv && seq > 0 && seq % a.S_p == 0;
+  TC tc;
+  int cpage = 0;
+  if (upd) {
+    cpage = a.pt[(size_t)b * a.pt_stride + n_b - 1];
+    tc.load(reinterpret_cast<const T*>(a.k) + ((size_t)cpage * a.H_kv + blockIdx.x) * (size_t)a.S_p * D,
+            a.S_p);
+  }
+  float* cred = smem + a.H_kv * D + a.cand_per_block + (NCH > 1 ? NCH * a.H_kv * D : 0);
+  auto centroid_done = [&]() {
+    if (!upd) return;
+    tc.reduce(cred, a.S_p);
+    __syncthreads();
+    if (tid < TC::S::SEGS)
+      TC::finish(cred, a.S_p, reinterpret_cast<T*>(a.cent_out) + ((size_t)cpage * a.H_kv + blockIdx.x) * D,
+                 tid);
+  };
+  if (c0 >= n_cand) {
+    centroid_done();
+    return;
+  }
   const int c1 = min(c0 + a.cand_per_block, n_cand);
   const int nc = c1 - c0;
 
@@ -272,6 +296,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       if (r1 < rows) consume(r1, tb);
     }
   }
+  centroid_done();
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
@@ -316,7 +341,8 @@ template <typename T, int D>
 hipError_t run_score(const ScoreArgs& a, int grid_x, hipStream_t s) {
   const int G = a.H_q / a.H_kv, nch = (G + 7) / 8;
   const size_t lds = (size_t)a.H_kv * D * sizeof(float) + (size_t)a.cand_per_block * sizeof(int32_t) +
-                     (nch > 1 ? (size_t)nch * a.H_kv * D * sizeof(float) : 0);
+                     (nch > 1 ? (size_t)nch * a.H_kv * D * sizeof(float) : 0) +
+                     (a.update_completed ? (size_t)CentroidShape<T, D>::RG * D * sizeof(float) : 0);
   hipLaunchKernelGGL((score_kernel<T, D>), dim3(grid_x, a.B), dim3(kScoreThreads), lds, s, a);
   return hipGetLastError();
 }

@@ -120,46 +120,13 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   // The page this step's token completed: its K tile rows are loaded now and
   // summed per row group after the scoring loop (the loads complete under
   // the scoring's), the groups are added at the end.
-  using CS = CentroidShape<T, D>;
-  constexpr int CP = (CS::THREADS + NT - 1) / NT;        // (row group, segment) pairs per thread
-  constexpr int CR = 64 / CS::RG;                        // rows per pair, S_p <= 64
+  using TC = TileCentroid<T, D, NT>;
   const bool upd = a.update_completed && seq > 0 && seq % SP == 0;
-  uint4 crow[CP][CR];
-  if (upd) {
-    const T* tile = reinterpret_cast<const T*>(a.d.k) + ((size_t)prow[n_b - 1] * s.H_kv + h) * SP * D;
-#pragma unroll
-    for (int c = 0; c < CP; ++c) {
-      const int pr = tid + c * NT, g = pr / CS::SEGS, sg = pr % CS::SEGS;
-#pragma unroll
-      for (int j = 0; j < CR; ++j)
-        if (pr < CS::THREADS && g + j * CS::RG < SP)
-          crow[c][j] = ld16(tile + (size_t)(g + j * CS::RG) * D + sg * CS::E);
-    }
-  }
+  TC tc;
+  if (upd) tc.load(reinterpret_cast<const T*>(a.d.k) + ((size_t)prow[n_b - 1] * s.H_kv + h) * SP * D, SP);
 
   if (scoring) score_head<T, D, NT>(s, h, n_cand, prow + a.n_bos, qbar, keys, sl);
-  if (upd) {
-#pragma unroll
-    for (int c = 0; c < CP; ++c) {
-      const int pr = tid + c * NT, g = pr / CS::SEGS, sg = pr % CS::SEGS;
-      if (pr < CS::THREADS) {
-        float part[CS::E];
-#pragma unroll
-        for (int e = 0; e < CS::E; ++e) part[e] = 0.f;
-#pragma unroll
-        for (int j = 0; j < CR; ++j) {
-          if (g + j * CS::RG < SP) {
-            float f[CS::E];
-            Vec16<T>::unpack(crow[c][j], f);
-#pragma unroll
-            for (int e = 0; e < CS::E; ++e) part[e] += f[e];
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < CS::E; ++e) cred[g][sg * CS::E + e] = part[e];
-      }
-    }
-  }
+  if (upd) tc.reduce(&cred[0][0], SP);
   const int count = select_pages<NT>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
                                      nullptr, list, sl);
   __syncthreads();
@@ -177,20 +144,9 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   int32_t* srow = a.sel + ((size_t)b * s.H_kv + h) * a.k_tot;
   auto epilogue = [&](int t, int nt) {
     for (int i = t; i < a.k_tot; i += nt) srow[i] = i < count ? list[i] : -1;
-    if (upd && t < CS::SEGS) {
-      // row groups added in order, then the scale: the order of centroid_segment()
-      float sum[CS::E];
-#pragma unroll
-      for (int e = 0; e < CS::E; ++e) sum[e] = 0.f;
-      for (int g = 0; g < CS::RG; ++g)
-#pragma unroll
-        for (int e = 0; e < CS::E; ++e) sum[e] += cred[g][t * CS::E + e];
-      const float inv = 1.0f / (float)SP;
-#pragma unroll
-      for (int e = 0; e < CS::E; ++e) sum[e] *= inv;
-      T* cp = reinterpret_cast<T*>(a.cent) + ((size_t)prow[n_b - 1] * s.H_kv + h) * D;
-      st16(cp + t * CS::E, Vec16<T>::pack(sum));
-    }
+    if (upd && t < TC::S::SEGS)
+      TC::finish(&cred[0][0], SP,
+                 reinterpret_cast<T*>(a.cent) + ((size_t)prow[n_b - 1] * s.H_kv + h) * D, t);
   };
   attend_pages<T, D, G, HS, PF, NW>(a.d, b, h, 0, 0, count, seq, page_at, epilogue);
 }
