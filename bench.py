@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-radix", action="store_true",
+                    help="skip the lossy radix top-k (vx_score_topk_radix) comparison")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer a few times (reference for HBM counters)")
     args = ap.parse_args()
@@ -343,6 +345,68 @@ def main():
     }
     log(f"separate calls: {separate['ms_per_step']:.4f} ms/step")
 
+    # ---------------- lossy radix top-k against the exact indexer
+    radix = None
+    if not args.no_radix:
+        rng = np.random.default_rng(w.seed + 17)
+        rnd = torch.from_numpy(rng.integers(0, 2 ** 32, size=w.batch * w.num_kv_heads,
+                                            dtype=np.uint64).astype(np.uint32).view(np.int32)).to(dev)
+        sel_r = torch.empty_like(sel)
+
+        def time_calls(pick):
+            for i in range(min(W_steps, 8)):
+                pick(i)()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n_sep):
+                pick(W_steps + i)()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n_sep
+
+        def recall(step_i):
+            """Mean over (request, KV head) of |lossy top-k & exact top-k| / |exact top-k|
+            (reserved pages, in both, left out)."""
+            s_ = step_i % T
+            e_tab, r_tab = sel.cpu().numpy(), sel_r.cpu().numpy()
+            vals = []
+            for b in range(w.batch):
+                n_b = -(-int(L_steps[s_][b]) // w.page_size)
+                res = set(range(min(w.n_bos, n_b))) | set(range(max(n_b - w.n_eos, 0), n_b))
+                for h in range(w.num_kv_heads):
+                    E = set(e_tab[b, h][e_tab[b, h] >= 0].tolist()) - res
+                    R = set(r_tab[b, h][r_tab[b, h] >= 0].tolist()) - res
+                    if E:
+                        vals.append(len(E & R) / len(E))
+            return float(np.mean(vals)), float(np.mean(np.array(vals) < 1.0))
+
+        radix = {"exact_indexer_ms": time_calls(lambda i: schedule(i)["idx"]), "levels": {}}
+        for levels in (1, 2):
+            prep = {}
+
+            def pick(i, levels=levels, prep=prep):
+                key = (i % nL, i % T)
+                if key not in prep:
+                    kv, bt, q = layers[key[0]]["kv"], batches[key[1]], layers[key[0]]["qs"][key[1]]
+                    prep[key] = vx.prepare_score_topk_radix(kv, bt, q, w.topk, w.n_bos, w.n_eos,
+                                                            levels, rnd, sel_r, ws_idx, stream)
+                return prep[key]
+            ms = time_calls(pick)
+            rec, frac = [], []
+            for i in range(min(nL * T, 8)):
+                schedule(i)["idx"]()
+                pick(i)()
+                torch.cuda.synchronize()
+                r_, f_ = recall(i)
+                rec.append(r_)
+                frac.append(f_)
+            radix["levels"][str(levels)] = {
+                "avg_ms": ms, "speedup_vs_exact": radix["exact_indexer_ms"] / ms,
+                "recall_at_k": float(np.mean(rec)),
+                "units_not_exact": float(np.mean(frac))}
+        log(f"radix top-k: {radix}")
+
     # ---------------- dense comparator
     dense = None
     if not args.no_dense:
@@ -405,6 +469,7 @@ def main():
         "launch_ms_p10_p50_p90_with_events": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
         "host_enqueue_us_per_step": enqueue * 1e6 / K_steps,
         "separate_calls": separate,
+        "radix_topk": radix,
         "dense": dense,
     }
     print(json.dumps(line), flush=True)

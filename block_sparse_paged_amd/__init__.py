@@ -31,7 +31,7 @@ VX_F32, VX_BF16 = 0, 1
 VX_OP_SCORE_TOPK, VX_OP_SPARSE_DECODE, VX_OP_FULL_DECODE, VX_OP_DECODE_STEP = 0, 1, 2, 3
 
 # Symbols include/vx.h declares (checked by the ABI tests).
-EXPORTS = ("vx_centroid_update", "vx_score_topk", "vx_sparse_paged_decode",
+EXPORTS = ("vx_centroid_update", "vx_score_topk", "vx_score_topk_radix", "vx_sparse_paged_decode",
            "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
            "vx_set_pages_per_split", "vx_status_string", "vx_version")
 
@@ -78,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     kvp, btp = P(PagedKVStruct), P(BatchStruct)
     lib.vx_centroid_update.argtypes = [kvp, VP, I32, VP]
     lib.vx_score_topk.argtypes = [kvp, btp, VP, I32, I32, I32, VP, VP, SZ, VP]
+    lib.vx_score_topk_radix.argtypes = [kvp, btp, VP, I32, I32, I32, I32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_paged_decode.argtypes = [kvp, btp, VP, VP, I32, F32, VP, VP, VP, SZ, VP]
     lib.vx_full_paged_decode.argtypes = [kvp, btp, VP, F32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_decode_step.argtypes = [kvp, btp, VP, I32, I32, I32, I32, F32, VP, VP, VP,
@@ -87,7 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_status_string.argtypes = [I32]
     lib.vx_status_string.restype = ctypes.c_char_p
     lib.vx_version.argtypes = []
-    for name in ("vx_centroid_update", "vx_score_topk", "vx_sparse_paged_decode",
+    for name in ("vx_centroid_update", "vx_score_topk", "vx_score_topk_radix",
+                 "vx_sparse_paged_decode",
                  "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
                  "vx_set_pages_per_split", "vx_version"):
         getattr(lib, name).restype = I32
@@ -194,6 +196,24 @@ def score_topk(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int
         _ptr(workspace), workspace.numel(), _stream(stream)), "vx_score_topk")
 
 
+def score_topk_radix(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
+                     n_eos: int, levels: int, rnd: torch.Tensor, sel: torch.Tensor,
+                     workspace: torch.Tensor, stream=None):
+    """vx_score_topk_radix: the lossy radix top-k (``levels`` histogram
+    levels, then the boundary bin's members by rank from ``rnd``) into sel.
+    ``rnd`` holds one random 32-bit word per (request, KV head) (int32 or
+    uint32 tensor of B * H_kv elements, read as uint32)."""
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    if rnd.device.type != "cuda" or not rnd.is_contiguous() or rnd.element_size() != 4 or \
+            rnd.dtype.is_floating_point:
+        raise ValueError("rnd must be a contiguous 32-bit integer CUDA tensor")
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_score_topk_radix(
+        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, levels, _ptr(rnd),
+        _ptr(sel), _ptr(workspace), workspace.numel(), _stream(stream)), "vx_score_topk_radix")
+
+
 def sparse_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sel: torch.Tensor,
                         sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
                         workspace: torch.Tensor, stream=None):
@@ -272,6 +292,18 @@ def prepare_score_topk(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, sel, wo
             _ptr(workspace), workspace.numel(), _stream(stream))
     return PreparedCall(lib.vx_score_topk, args, "vx_score_topk",
                         (kvs, bs, kv, batch, q, sel, workspace))
+
+
+def prepare_score_topk_radix(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, levels, rnd,
+                             sel, workspace, stream=None) -> PreparedCall:
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, levels, _ptr(rnd),
+            _ptr(sel), _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall(lib.vx_score_topk_radix, args, "vx_score_topk_radix",
+                        (kvs, bs, kv, batch, q, rnd, sel, workspace))
 
 
 def prepare_sparse_paged_decode(kv: PagedKV, batch: Batch, q, sel, sm_scale, out, lse,

@@ -241,7 +241,8 @@ hipError_t launch_completed_centroids(const vx_paged_kv* kv, const vx_batch* bat
 vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                           int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
                           void* workspace, size_t workspace_bytes, hipStream_t stream,
-                          bool update_completed = false) {
+                          bool update_completed = false, int levels = 0,
+                          const uint32_t* rnd = nullptr) {
   vx_status st = check_kv(kv);
   if (st != VX_OK) return st;
   if ((st = check_batch(kv, batch)) != VX_OK) return st;
@@ -276,6 +277,8 @@ vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const vo
   t.n_bos = n_bos;
   t.n_eos = n_eos;
   t.k_tot = k_tot;
+  t.levels = levels;
+  t.rnd = rnd;
 
   // One block per (request, KV head) when there are enough of them to fill
   // the GPU (or the whole problem is tiny) and the candidate keys fit in LDS.
@@ -429,6 +432,21 @@ vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return score_topk_impl(kv, batch, q, topk, n_bos, n_eos, sel, workspace, workspace_bytes,
                          stream);
+}
+
+vx_status vx_score_topk_radix(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                              int32_t topk, int32_t n_bos, int32_t n_eos, int32_t levels,
+                              const uint32_t* rnd, int32_t* sel, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (levels != 1 && levels != 2) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch > 0 && !rnd) return VX_ERR_INVALID_ARGUMENT;
+  // the early stop works on candidates held in registers by 512-thread blocks
+  if (max_pages_eff(kv, batch) - n_bos - n_eos > 4 * kSelRegChunks * 512) return VX_ERR_UNSUPPORTED;
+  return score_topk_impl(kv, batch, q, topk, n_bos, n_eos, sel, workspace, workspace_bytes,
+                         stream, false, levels, rnd);
 }
 
 vx_status vx_sparse_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, const void* q,

@@ -42,12 +42,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeArgs a) {
     __syncthreads();
     if (n_cand > a.topk && a.topk > 0) {
       const float* sc = a.scores + ((size_t)b * a.H_kv + h) * a.score_stride;
-      for (int i0 = tid; i0 < n_cand; i0 += 8 * NT) {
-        float v[8];
+      constexpr int kIn = 16;          // score loads in flight per thread
+      for (int i0 = tid; i0 < n_cand; i0 += kIn * NT) {
+        float v[kIn];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = sc[min(i0 + j * NT, n_cand - 1)];
+        for (int j = 0; j < kIn; ++j) v[j] = sc[min(i0 + j * NT, n_cand - 1)];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kIn; ++j) {
           const int i = i0 + j * NT;
           if (i < n_cand) {
             const uint32_t k = order_key(v[j]);

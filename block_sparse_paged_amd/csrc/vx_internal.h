@@ -22,6 +22,10 @@ struct CentroidArgs {
   int32_t pt_stride, max_tokens;
 };
 
+// 16-byte chunks of keys a thread keeps in registers during a selection; the
+// lossy radix top-k stops early only for candidates held that way.
+constexpr int kSelRegChunks = 4;
+
 // Most rows of a page-head tile whose centroid a longer kernel computes.
 constexpr int kMaxTileRows = 64;
 
@@ -48,6 +52,10 @@ struct TopkArgs {
   int32_t* sel;           // [B, H_kv, k_tot]
   int32_t B, H_kv, S_p, score_stride, max_tokens;
   int32_t topk, n_bos, n_eos, k_tot;
+  // lossy radix top-k: histogram levels before the early stop (0: exact) and
+  // one random word per (request, KV head) [B, H_kv]
+  int32_t levels;
+  const uint32_t* rnd;
 };
 
 struct DecodeArgs {

@@ -62,7 +62,8 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs 
 
   if (scoring) score_head<T, D, kFusedThreads>(a, h, n_cand, phys, qbar, keys, sl);
   select_pages<kFusedThreads>(keys, n_cand, n_b, t.topk, t.n_bos, t.n_eos, t.k_tot,
-                              t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, nullptr, sl);
+                              t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, nullptr, sl, t.levels,
+                              t.rnd ? t.rnd[(size_t)b * t.H_kv + h] : 0u);
 }
 
 // ---------------------------------------------------------------- split
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
   }
   select_pages<kTopkThreads>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
-                             a.sel + (size_t)bh * a.k_tot, nullptr, sl);
+                             a.sel + (size_t)bh * a.k_tot, nullptr, sl, a.levels,
+                             a.rnd ? a.rnd[bh] : 0u);
 }
 
 template <typename T, int D>

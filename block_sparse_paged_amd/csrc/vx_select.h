@@ -37,8 +37,6 @@ constexpr int kSelShift0 = 32 - kSelBits;     // level-0 bin of a key: key >> 22
 __device__ __forceinline__ int sel_slot(int i) { return i + (i >> 4) * 4; }
 constexpr int kSelHistWords = kSelBins + kSelBins / 4;
 
-// 16-byte chunks of keys a thread keeps in registers during a selection.
-constexpr int kSelRegChunks = 4;
 
 // LDS of one selection (NT threads): two histograms (levels alternate).
 template <int NT>
@@ -121,10 +119,18 @@ __device__ __forceinline__ void find_bin(const int* hist, int remaining, int& ds
 //          order-preserving keys of candidates n_bos.. (in page order), each
 //          counted by select_count; keys and counts visible to every thread
 //   S      select_init()ed
+// With max_levels > 0 the selection stops after that many histogram levels
+// (the lossy radix top-k with early termination of the Vortex article,
+// section "A dual-stage programmable abstraction"): when the boundary bin of
+// the last level is not taken whole, its members are taken by rank in page
+// order, cyclically from rank rnd mod (members), instead of by key.  This
+// early stop applies when the keys are held in registers (n_cand <= NT *
+// 4 * kSelRegChunks); larger inputs are selected exactly.
 template <int NT>
 __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, int n_b, int topk,
                                             int n_bos, int n_eos, int k_tot, int32_t* out,
-                                            int32_t* lds_out, SelectLds<NT>& S) {
+                                            int32_t* lds_out, SelectLds<NT>& S, int max_levels = 0,
+                                            uint32_t rnd = 0u) {
   const int tid = threadIdx.x;
   // Thread tid owns candidates [c0, c0 + 4 nch), nch a power of two, as nch
   // 16-byte chunks of keys.  Lanes 4a .. 4a+3 take their chunks starting at
@@ -144,6 +150,10 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
   // candidate c is taken iff keys[c] > thr_key || (keys[c] == thr_key && c <= thr_idx)
   uint32_t thr_key = 0u;
   int thr_idx = INT_MAX;                                  // all candidates
+  // early stop: keys in [bin_lo, bin_hi] are taken by rank instead
+  bool early = false;
+  uint32_t bin_lo = 0u, bin_hi = 0u;
+  int bin_take = 0, bin_n = 0, bin_r0 = 0;
   if (n_cand > topk && topk == 0) {
     thr_key = 0xFFFFFFFFu;                                // none of them
     thr_idx = -1;
@@ -200,6 +210,22 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
         thr_key = lo;
         break;
       }
+      if (max_levels > 0 && level + 1 >= max_levels && in_regs) {
+        early = true;                  // keys above the bin, then members by rank
+        bin_lo = lo;
+        bin_hi = lo + span;
+        bin_take = remaining;
+        bin_n = cnt;
+        bin_r0 = (int)(rnd % (uint32_t)cnt);
+        if (bin_hi == 0xFFFFFFFFu) {   // no key lies above the bin
+          thr_key = 0xFFFFFFFFu;
+          thr_idx = -1;
+        } else {                       // every key above the bin
+          thr_key = bin_hi + 1u;
+          thr_idx = INT_MAX;
+        }
+        break;
+      }
       if (span == 0) {                 // cnt equal keys: the remaining-th in page order
         const int per = (n_cand + NT - 1) / NT;
         const int e0 = min(tid * per, n_cand), e1 = min(e0 + per, n_cand);
@@ -247,6 +273,7 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
   unsigned long long m0 = 0ull;
   int n_take = 0;
   if (in_regs) {
+    unsigned long long mem = 0ull;      // early stop: members of the boundary bin
 #pragma unroll
     for (int jj = 0; jj < kSelRegChunks; ++jj) {
       if (jj < nch) {
@@ -254,6 +281,23 @@ __device__ __forceinline__ int select_pages(const uint32_t* keys, int n_cand, in
         const unsigned t = taken(kr[jj].x, c) | taken(kr[jj].y, c + 1) << 1 |
                            taken(kr[jj].z, c + 2) << 2 | taken(kr[jj].w, c + 3) << 3;
         m0 |= (unsigned long long)t << (c - c0);
+        if (early) {
+          auto in_bin = [&](uint32_t k, int cc) { return cc < n_cand && k >= bin_lo && k <= bin_hi; };
+          const unsigned u = in_bin(kr[jj].x, c) | in_bin(kr[jj].y, c + 1) << 1 |
+                             in_bin(kr[jj].z, c + 2) << 2 | in_bin(kr[jj].w, c + 3) << 3;
+          mem |= (unsigned long long)u << (c - c0);
+        }
+      }
+    }
+    if (early) {
+      // member of page-order rank rho is taken iff (rho - r0) mod n < take
+      int mtot;
+      int rho = block_exclusive_scan<NT>(__popcll(mem), S.wsum[0], &mtot);
+      while (mem) {
+        const int e = __builtin_ctzll(mem);
+        if ((rho - bin_r0 + bin_n) % bin_n < bin_take) m0 |= 1ull << e;
+        ++rho;
+        mem &= mem - 1;
       }
     }
     n_take = __popcll(m0);

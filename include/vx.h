@@ -155,6 +155,30 @@ vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void
                         int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Lossy indexer: the "stochastic radix top-k" with early termination (Vortex
+ * article, section "A dual-stage programmable abstraction": a lossy radix
+ * top-k that stops early, trading a little exactness for indexing speed).
+ * The pages give no further detail; this library's reading:
+ *   keys      = order-preserving uint32 of the fp32 scores of vx_score_topk
+ *               (-0 and +0 equal)
+ *   level 0   = histogram of the top 10 key bits; level 1 (levels == 2)
+ *               splits the boundary bin of level 0 by the next 10 bits.
+ *   After `levels` levels, with A candidates in bins above the boundary bin
+ *   and N in it (A < topk <= A + N): every candidate above it is taken, and
+ *   of the bin's members, listed in ascending page order with ranks
+ *   0 .. N-1, those with (rank - rnd[b, h] mod N) mod N < topk - A.  When
+ *   the boundary bin is taken whole (A + N == topk) the result equals
+ *   vx_score_topk's.  Reserved pages, output order and padding as there.
+ *   levels     1 or 2 (VX_ERR_INVALID_ARGUMENT otherwise)
+ *   rnd        device uint32 [B, H_kv]: one random word per (request, KV
+ *              head), drawn by the caller (the "stochastic" part); read only
+ * Candidates per request are limited to 8192 pages (VX_ERR_UNSUPPORTED).
+ * Other arguments, workspace and errors as vx_score_topk. */
+vx_status vx_score_topk_radix(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                              int32_t topk, int32_t n_bos, int32_t n_eos, int32_t levels,
+                              const uint32_t* rnd, int32_t* sel, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Sparse attention over the selected pages (article, "A dual-stage
  * programmable abstraction": after selecting the top-k blocks the system
  * performs the actual attention on them).

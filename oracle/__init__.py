@@ -5,4 +5,8 @@ benchmark's CPU-baseline leg.  The GPU library never imports it.
 """
 
 from .block_topk import *  # noqa: F401,F403
-from .block_topk import __all__  # noqa: F401
+from .block_topk import __all__ as _exact_all
+from .radix_topk import *  # noqa: F401,F403
+from .radix_topk import __all__ as _radix_all
+
+__all__ = list(_exact_all) + list(_radix_all)
