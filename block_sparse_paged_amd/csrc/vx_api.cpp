@@ -335,7 +335,7 @@ hipError_t launch_completed_centroids(const vx_paged_kv* kv, const vx_batch* bat
 
 // The split indexer's scoring kernel alone: fp32 scores [B, H_kv, mp] into
 // `scores`.  With update_completed it also writes the completed pages'
-// centroids (in the kernel when it has a block for every KV head, else with
+// centroids (in the kernel when each block's share of a page fits, else with
 // the centroid kernel first).
 hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                               int32_t n_bos, int32_t n_eos, float* scores, bool update_completed,
@@ -367,7 +367,8 @@ hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, cons
     s.cand_per_block = cpb;
     const int grid_x = ceil_div(max_cand, cpb);
     if (update_completed) {
-      if (grid_x >= kv->num_kv_heads && kv->page_size <= kMaxTileRows) {
+      if (kv->page_size <= kMaxTileRows &&
+          score_centroid_fits(kv->dtype, kv->head_dim_qk, kv->num_kv_heads, grid_x)) {
         s.k = kv->k_cache;
         s.cent_out = kv->centroids;
         s.update_completed = 1;

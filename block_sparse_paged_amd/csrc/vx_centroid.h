@@ -107,4 +107,71 @@ struct TileCentroid {
   }
 };
 
+// Part of the centroid rows of one page computed inside a longer kernel of NT
+// threads, again in the centroid kernel's order: the block takes units
+// [u0, u0 + nu) of the page's (KV head, 16-byte segment) pairs (unit u: head
+// u / SEGS, segment u % SEGS), so that the blocks of a request can share a
+// page without combining partial sums.  Thread t takes (unit, row group)
+// pairs t, t + NT, ... (at most CP of them); load() issues their rows early,
+// reduce() sums each pair into LDS `red` [nu * RG][E] later, and after a
+// barrier finish() completes unit u0 + t for t < nu.
+template <typename T, int D, int NT, int CP>
+struct SegmentCentroid {
+  using S = CentroidShape<T, D>;
+  static constexpr int CR = (kMaxTileRows + S::RG - 1) / S::RG;       // rows per pair
+  uint4 rows[CP][CR];
+
+  // page: the page's K rows [H_kv][S_p][D]
+  __device__ __forceinline__ void load(const T* page, int S_p, int u0, int nu) {
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      const int pr = threadIdx.x + c * NT;
+      const int u = u0 + pr / S::RG, g = pr % S::RG;
+      const int h = u / S::SEGS, sg = u % S::SEGS;
+#pragma unroll
+      for (int j = 0; j < CR; ++j)
+        if (pr < nu * S::RG && g + j * S::RG < S_p)
+          rows[c][j] = ld16(page + ((size_t)h * S_p + g + j * S::RG) * D + sg * S::E);
+    }
+  }
+
+  __device__ __forceinline__ void reduce(float* red, int S_p, int nu) const {
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      const int pr = threadIdx.x + c * NT, g = pr % S::RG;
+      if (pr < nu * S::RG) {
+        float part[S::E];
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) part[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < CR; ++j) {
+          if (g + j * S::RG < S_p) {
+            float f[S::E];
+            Vec16<T>::unpack(rows[c][j], f);
+#pragma unroll
+            for (int e = 0; e < S::E; ++e) part[e] += f[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) red[pr * S::E + e] = part[e];
+      }
+    }
+  }
+
+  // cent: the page's centroid rows [H_kv][D]
+  static __device__ __forceinline__ void finish(const float* red, int S_p, T* cent, int u0, int t) {
+    const int u = u0 + t, h = u / S::SEGS, sg = u % S::SEGS;
+    float sum[S::E];
+#pragma unroll
+    for (int e = 0; e < S::E; ++e) sum[e] = 0.f;
+    for (int g = 0; g < S::RG; ++g)
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) sum[e] += red[(t * S::RG + g) * S::E + e];
+    const float inv = 1.0f / (float)S_p;
+#pragma unroll
+    for (int e = 0; e < S::E; ++e) sum[e] *= inv;
+    st16(cent + (size_t)h * D + sg * S::E, Vec16<T>::pack(sum));
+  }
+};
+
 }  // namespace vx

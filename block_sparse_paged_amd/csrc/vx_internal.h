@@ -38,9 +38,9 @@ struct ScoreArgs {
   int32_t B, H_q, H_kv, D, S_p, pt_stride, score_stride, max_tokens;
   int32_t n_bos, n_eos;
   int32_t cand_per_block;
-  // split scorer only: when set, blocks x < H_kv also write the centroid of
-  // KV head x of the page each request's latest token completed (that page
-  // is reserved, never a candidate)
+  // split scorer only: when set, the blocks of each request also write the
+  // centroid rows of the page its latest token completed, each block a share
+  // of the (KV head, segment) units (that page is reserved, never a candidate)
   const void* k;          // [P, H_kv, S_p, D]
   void* cent_out;         // the centroid table, written
   int32_t update_completed;
@@ -107,6 +107,9 @@ struct CombineArgs {
 
 hipError_t launch_centroid(int dtype, const CentroidArgs& a, hipStream_t s);
 hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s);
+// Whether a split-scorer launch of grid_x blocks per request can also write
+// the completed pages' centroids (each block's share of the page's rows fits).
+bool score_centroid_fits(int dtype, int D, int H_kv, int grid_x);
 hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s);
 // One block per (request, KV head) scores and selects (rows of <= 64 lanes).
 bool fused_indexer_supported(int dtype, int D);

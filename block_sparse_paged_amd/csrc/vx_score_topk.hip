@@ -34,6 +34,9 @@ constexpr int kScoreThreads = 512;
 constexpr int kTopkThreads = 512;
 constexpr int kFusedThreads = 512;
 constexpr int kLoadsInFlight = 16;   // wave-loads issued before the first is used
+// (KV head, segment, row group) triples of a completed page one scoring
+// block takes at most (two per thread)
+constexpr int kScoreCentroidPairs = 2 * kScoreThreads;
 
 // ---------------------------------------------------------------- fused
 template <typename T, int D>
@@ -125,25 +128,26 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
   const int n_cand = n_b - a.n_bos - a.n_eos;
-  // the completed page's centroid (blocks x < H_kv, head x): rows loaded now,
-  // summed after the scoring
-  using TC = TileCentroid<T, D, kScoreThreads>;
-  const bool upd = a.update_completed && (int)blockIdx.x < a.H_kv && seq > 0 && seq % a.S_p == 0;
-  TC tc;
+  // the completed page's centroid rows, shared by the request's blocks by
+  // (KV head, segment) units: rows loaded now, summed after the scoring
+  using SC = SegmentCentroid<T, D, kScoreThreads, kScoreCentroidPairs / kScoreThreads>;
+  const int n_units = a.H_kv * SC::S::SEGS;
+  const int u0 = (int)((long long)blockIdx.x * n_units / gridDim.x);
+  const int nu = (int)((long long)(blockIdx.x + 1) * n_units / gridDim.x) - u0;
+  const bool upd = a.update_completed && nu > 0 && seq > 0 && seq % a.S_p == 0;
+  SC sc;
   int cpage = 0;
   if (upd) {
     cpage = a.pt[(size_t)b * a.pt_stride + n_b - 1];
-    tc.load(reinterpret_cast<const T*>(a.k) + ((size_t)cpage * a.H_kv + blockIdx.x) * (size_t)a.S_p * D,
-            a.S_p);
+    sc.load(reinterpret_cast<const T*>(a.k) + (size_t)cpage * a.H_kv * a.S_p * D, a.S_p, u0, nu);
   }
   float* cred = smem + a.H_kv * D + a.cand_per_block + (NCH > 1 ? NCH * a.H_kv * D : 0);
   auto centroid_done = [&]() {
     if (!upd) return;
-    tc.reduce(cred, a.S_p);
+    sc.reduce(cred, a.S_p, nu);
     __syncthreads();
-    if (tid < TC::S::SEGS)
-      TC::finish(cred, a.S_p, reinterpret_cast<T*>(a.cent_out) + ((size_t)cpage * a.H_kv + blockIdx.x) * D,
-                 tid);
+    if (tid < nu)
+      SC::finish(cred, a.S_p, reinterpret_cast<T*>(a.cent_out) + (size_t)cpage * a.H_kv * D, u0, tid);
   };
   if (c0 >= n_cand) {
     centroid_done();
@@ -339,12 +343,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
                              a.rnd ? a.rnd[bh] : 0u);
 }
 
+// LDS of the completed-page centroid share of the busiest scoring block.
+template <typename T, int D>
+size_t score_centroid_lds(int H_kv, int grid_x) {
+  using S = CentroidShape<T, D>;
+  const int per_block = (H_kv * S::SEGS + grid_x - 1) / grid_x;
+  return (size_t)per_block * S::RG * S::E * sizeof(float);
+}
+
 template <typename T, int D>
 hipError_t run_score(const ScoreArgs& a, int grid_x, hipStream_t s) {
   const int G = a.H_q / a.H_kv, nch = (G + 7) / 8;
   const size_t lds = (size_t)a.H_kv * D * sizeof(float) + (size_t)a.cand_per_block * sizeof(int32_t) +
                      (nch > 1 ? (size_t)nch * a.H_kv * D * sizeof(float) : 0) +
-                     (a.update_completed ? (size_t)CentroidShape<T, D>::RG * D * sizeof(float) : 0);
+                     (a.update_completed ? score_centroid_lds<T, D>(a.H_kv, grid_x) : 0);
   hipLaunchKernelGGL((score_kernel<T, D>), dim3(grid_x, a.B), dim3(kScoreThreads), lds, s, a);
   return hipGetLastError();
 }
@@ -361,6 +373,25 @@ hipError_t run_fused(const ScoreArgs& a, const TopkArgs& t, hipStream_t s) {
 
 bool fused_indexer_supported(int dtype, int D) {
   return (dtype == 0 && (D == 64 || D == 128)) || (dtype == 1 && (D == 64 || D == 128));
+}
+
+template <typename T, int D>
+bool centroid_share_fits(int H_kv, int grid_x) {
+  using S = CentroidShape<T, D>;
+  return (H_kv * S::SEGS + grid_x - 1) / grid_x * S::RG <= kScoreCentroidPairs;
+}
+
+bool score_centroid_fits(int dtype, int D, int H_kv, int grid_x) {
+  if (grid_x < 1) return false;
+  if (dtype == 0) {
+    if (D == 64) return centroid_share_fits<float, 64>(H_kv, grid_x);
+    if (D == 128) return centroid_share_fits<float, 128>(H_kv, grid_x);
+  } else {
+    if (D == 64) return centroid_share_fits<bf16_t, 64>(H_kv, grid_x);
+    if (D == 128) return centroid_share_fits<bf16_t, 128>(H_kv, grid_x);
+    if (D == 576) return centroid_share_fits<bf16_t, 576>(H_kv, grid_x);
+  }
+  return false;
 }
 
 hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s) {
