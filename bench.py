@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip timing the write path (vx_append_kv)")
     ap.add_argument("--no-radix", action="store_true",
                     help="skip the lossy radix top-k (vx_score_topk_radix) comparison")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -407,6 +409,54 @@ def main():
                 "units_not_exact": float(np.mean(frac))}
         log(f"radix top-k: {radix}")
 
+    # ---------------- the write path: vx_append_kv (rows rewritten with their own
+    # values, so the layers stay as they are)
+    append = None
+    if not args.no_append:
+        lay0, s0 = layers[0], 0
+        L0 = np.asarray(L_steps[s0], dtype=np.int64)
+        e = 2 if w.dtype == "bf16" else 4
+        K0 = lay0["K"]
+        V0 = lay0["V"]
+        append = {}
+        for n in (1, 64):
+            pos = np.concatenate([np.arange(max(int(Lb) - n, 0), int(Lb)) for Lb in L0])
+            req = np.concatenate([np.full(min(n, int(Lb)), b) for b, Lb in enumerate(L0)])
+            pages = torch.from_numpy(lay.page_table[req, pos // w.page_size].astype(np.int64)).to(dev)
+            slots = torch.from_numpy((pos % w.page_size).astype(np.int64)).to(dev)
+            k_src = K0[pages, :, slots].contiguous()
+            v_src = None if V0 is None else V0[pages, :, slots].contiguous()
+            n_req = np.minimum(n, L0)
+            starts = torch.from_numpy(np.concatenate([[0], np.cumsum(n_req)[:-1]]).astype(np.int32)).to(dev)
+            n_new = torch.from_numpy(n_req.astype(np.int32)).to(dev)
+            call = vx.prepare_append_kv(lay0["kv"], batches[s0], k_src, v_src, starts, n_new, n,
+                                        True, stream)
+            # algorithmic bytes: new rows read and written; each filled page's
+            # old rows read and its centroid row written
+            dv = 0 if V0 is None else w.head_dim_v
+            b_rows = 2 * len(pos) * w.num_kv_heads * (w.head_dim_qk + dv) * e
+            b_cent = 0
+            for Lb, nb in zip(L0, n_req):
+                first = int(Lb) - int(nb)
+                for p_ in range(first // w.page_size, int(Lb) // w.page_size):
+                    old = max(first - p_ * w.page_size, 0)
+                    b_cent += w.num_kv_heads * w.head_dim_qk * e * (old + 1)
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 200
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            append["decode_1_token" if n == 1 else f"write_{n}_tokens"] = {
+                "tokens_per_request": n, "avg_ms": ms, "bytes": int(b_rows + b_cent),
+                "gbps": (b_rows + b_cent) / (ms * 1e-3) / 1e9}
+        log(f"append: {append}")
+
     # ---------------- dense comparator
     dense = None
     if not args.no_dense:
@@ -470,6 +520,7 @@ def main():
         "host_enqueue_us_per_step": enqueue * 1e6 / K_steps,
         "separate_calls": separate,
         "radix_topk": radix,
+        "append_kv": append,
         "dense": dense,
     }
     print(json.dumps(line), flush=True)

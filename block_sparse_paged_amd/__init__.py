@@ -31,7 +31,8 @@ VX_F32, VX_BF16 = 0, 1
 VX_OP_SCORE_TOPK, VX_OP_SPARSE_DECODE, VX_OP_FULL_DECODE, VX_OP_DECODE_STEP = 0, 1, 2, 3
 
 # Symbols include/vx.h declares (checked by the ABI tests).
-EXPORTS = ("vx_centroid_update", "vx_score_topk", "vx_score_topk_radix", "vx_sparse_paged_decode",
+EXPORTS = ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
+           "vx_sparse_paged_decode",
            "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
            "vx_set_pages_per_split", "vx_status_string", "vx_version")
 
@@ -77,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            ctypes.c_float, ctypes.c_void_p)
     kvp, btp = P(PagedKVStruct), P(BatchStruct)
     lib.vx_centroid_update.argtypes = [kvp, VP, I32, VP]
+    lib.vx_append_kv.argtypes = [kvp, btp, VP, VP, VP, VP, I32, I32, I32, VP]
     lib.vx_score_topk.argtypes = [kvp, btp, VP, I32, I32, I32, VP, VP, SZ, VP]
     lib.vx_score_topk_radix.argtypes = [kvp, btp, VP, I32, I32, I32, I32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_paged_decode.argtypes = [kvp, btp, VP, VP, I32, F32, VP, VP, VP, SZ, VP]
@@ -88,7 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_status_string.argtypes = [I32]
     lib.vx_status_string.restype = ctypes.c_char_p
     lib.vx_version.argtypes = []
-    for name in ("vx_centroid_update", "vx_score_topk", "vx_score_topk_radix",
+    for name in ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
                  "vx_sparse_paged_decode",
                  "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
                  "vx_set_pages_per_split", "vx_version"):
@@ -183,6 +185,35 @@ def centroid_update(kv: PagedKV, page_ids: torch.Tensor, stream=None):
     _check(load_library().vx_centroid_update(ctypes.byref(kvs), _ptr(page_ids),
                                              page_ids.numel(), _stream(stream)),
            "vx_centroid_update")
+
+
+def append_kv(kv: PagedKV, batch: Batch, k_src: torch.Tensor, v_src: Optional[torch.Tensor],
+              src_start: torch.Tensor, n_new: torch.Tensor, max_new: int,
+              update_centroids: bool = True, stream=None):
+    """vx_append_kv: request b's last n_new[b] tokens (lengths from batch,
+    after the write) from rows src_start[b].. of k_src / v_src into the
+    cache, with the centroids of the pages the write fills."""
+    _need(k_src, "k_src")
+    if v_src is not None:
+        _need(v_src, "v_src")
+    _need(src_start, "src_start", torch.int32)
+    _need(n_new, "n_new", torch.int32)
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_append_kv(
+        ctypes.byref(kvs), ctypes.byref(bs), _ptr(k_src), _ptr(v_src), _ptr(src_start),
+        _ptr(n_new), k_src.shape[0], int(max_new), int(bool(update_centroids)),
+        _stream(stream)), "vx_append_kv")
+
+
+def prepare_append_kv(kv: PagedKV, batch: Batch, k_src, v_src, src_start, n_new, max_new,
+                      update_centroids=True, stream=None) -> "PreparedCall":
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(k_src), _ptr(v_src), _ptr(src_start),
+            _ptr(n_new), k_src.shape[0], int(max_new), int(bool(update_centroids)),
+            _stream(stream))
+    return PreparedCall(lib.vx_append_kv, args, "vx_append_kv",
+                        (kvs, bs, kv, batch, k_src, v_src, src_start, n_new))
 
 
 def score_topk(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,

@@ -428,6 +428,46 @@ vx_status vx_centroid_update(const vx_paged_kv* kv, const int32_t* page_ids, int
   return hip_status(launch_centroid(kv->dtype, a, stream));
 }
 
+vx_status vx_append_kv(const vx_paged_kv* kv, const vx_batch* batch, const void* k_src,
+                       const void* v_src, const int32_t* src_start, const int32_t* n_new,
+                       int32_t n_src_rows, int32_t max_new, int32_t update_centroids,
+                       hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (max_new < 0 || n_src_rows < 0) return VX_ERR_INVALID_ARGUMENT;
+  if (update_centroids != 0 && update_centroids != 1) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0 || max_new == 0) return VX_OK;
+  if (!k_src || !src_start || !n_new || !kv->k_cache || !batch->page_table ||
+      !batch->seq_lens || (update_centroids && !kv->centroids))
+    return VX_ERR_INVALID_ARGUMENT;
+  if (kv->v_aliases_k ? v_src != nullptr : (!v_src || !kv->v_cache))
+    return VX_ERR_INVALID_ARGUMENT;
+  AppendArgs a{};
+  a.k = const_cast<void*>(kv->k_cache);
+  a.v = kv->v_aliases_k ? nullptr : const_cast<void*>(kv->v_cache);
+  a.cent = kv->centroids;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.src_start = src_start;
+  a.n_new = n_new;
+  a.pt = batch->page_table;
+  a.seq_lens = batch->seq_lens;
+  a.B = batch->batch;
+  a.H_kv = kv->num_kv_heads;
+  a.S_p = kv->page_size;
+  a.Dq = kv->head_dim_qk;
+  a.Dv = kv->head_dim_v;
+  a.pt_stride = batch->max_pages_per_req;
+  a.max_tokens = batch->max_seq_len;
+  a.max_new = max_new;
+  a.n_src_rows = n_src_rows;
+  a.update = update_centroids;
+  const long long pages = (long long)ceil_div(max_new, kv->page_size) + 1;
+  if (pages > 0x7fffffffLL) return VX_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_append(kv->dtype, a, (int)pages, stream));
+}
+
 vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                         int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -106,6 +106,21 @@ struct CombineArgs {
 };
 
 hipError_t launch_centroid(int dtype, const CentroidArgs& a, hipStream_t s);
+
+struct AppendArgs {
+  void* k;                // [P, H_kv, S_p, Dq]
+  void* v;                // [P, H_kv, S_p, Dv], or nullptr when V is the leading part of K
+  void* cent;             // [P, H_kv, Dq]
+  const void* k_src;      // [n_src_rows, H_kv, Dq]
+  const void* v_src;      // [n_src_rows, H_kv, Dv] (v != nullptr)
+  const int32_t* src_start;   // [B] source row of request b's first new token
+  const int32_t* n_new;       // [B] new tokens of request b (its last ones)
+  const int32_t* pt;          // [B, pt_stride]
+  const int32_t* seq_lens;    // [B] lengths after the write
+  int32_t B, H_kv, S_p, Dq, Dv, pt_stride, max_tokens, max_new, n_src_rows, update;
+};
+// grid x: pages a request's write can touch, ceil(max_new / S_p) + 1
+hipError_t launch_append(int dtype, const AppendArgs& a, int pages_per_req, hipStream_t s);
 hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s);
 // Whether a split-scorer launch of grid_x blocks per request can also write
 // the completed pages' centroids (each block's share of the page's rows fits).

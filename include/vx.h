@@ -128,6 +128,31 @@ typedef struct {
 vx_status vx_centroid_update(const vx_paged_kv* kv, const int32_t* page_ids,
                              int32_t n_ids, hipStream_t stream);
 
+/* The write path beside the decode step: new tokens' K/V rows into their
+ * pages, with the centroid of every page the write fills (article, "A
+ * dual-stage programmable abstraction": summaries are made while the cache is
+ * built; README "Quick Example": a page's centroid once it is full).  One
+ * token per request is the decode append; many are a prefill write.
+ *
+ * For request b with L = seq_lens[b] (the length after the write) and
+ * n = min(n_new[b], max_new, L) new tokens at positions L-n .. L-1:
+ *   K[page_table[b, pos / S_p], h, pos % S_p, :] = k_src[src_start[b] + pos - (L-n), h, :]
+ *   V likewise from v_src (skipped when v_aliases_k)
+ * and, with update_centroids, for every page p whose last position lies in
+ * [L-n, L): centroids[page_table[b, p], h, :] as vx_centroid_update writes it
+ * (the same bits).  Rows outside [0, n_src_rows) are not read or written.
+ *   k_src      device [n_src_rows, H_kv, D_qk], dtype
+ *   v_src      device [n_src_rows, H_kv, D_v], dtype; NULL when v_aliases_k
+ *   src_start  device int32 [B]; n_new device int32 [B]
+ *   max_new    host bound on n_new (sets the launch); 0 launches nothing
+ *   update_centroids  0 or 1
+ * kv->k_cache and kv->v_cache are written (the rows above only), as is the
+ * centroid table (its rows above only). */
+vx_status vx_append_kv(const vx_paged_kv* kv, const vx_batch* batch, const void* k_src,
+                       const void* v_src, const int32_t* src_start, const int32_t* n_new,
+                       int32_t n_src_rows, int32_t max_new, int32_t update_centroids,
+                       hipStream_t stream);
+
 /* Query-dependent indexer (README "Quick Example": mean of the query over
  * heads, GeMV against the centroids, topK into the page index structure;
  * README "Using Your Sparse Attention with SGLang": top-k value and the
