@@ -607,15 +607,17 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
   // Otherwise: the indexer (with the completed pages' centroids), then
   // attention.
   // The split scorer's scores are selected from inside the split decode
-  // kernel (no top-k launch) when its keys fit in LDS beside the attention.
+  // kernel, or the MLA decode kernel (no top-k launch), when its keys fit in
+  // LDS beside the attention.
   const int max_cand = std::max(mp - n_bos - n_eos, 0);
   const bool split_scorer = !(fused_indexer_supported(kv->dtype, kv->head_dim_qk) &&
                               mp <= kFusedMaxPages &&
                               (units >= kNumCUs / 2 || units * mp <= 4096));
   const size_t sel_lds = (size_t)(round4(mp) + k_tot) * 4 + kSelectLdsBytes +
                          attention_lds_bytes(kv->head_dim_qk, G);
-  if (!is_mla(kv) && split_scorer && max_cand > topk && topk > 0 &&
-      sel_lds <= max_lds_per_block()) {
+  const bool select_fits = is_mla(kv) ? mla_select_fits(mp, k_tot)
+                                      : sel_lds <= max_lds_per_block();
+  if (split_scorer && max_cand > topk && topk > 0 && select_fits) {
     float* scores = reinterpret_cast<float*>(workspace);
     if (launch_split_score(kv, batch, q, n_bos, n_eos, scores, update_completed != 0, stream) !=
         hipSuccess)

@@ -20,8 +20,14 @@
 //     128w .. 128w+127 (4 tiles of 32); P is already in the B operand layout
 //     in registers; V^T is read from the K tile in LDS (so HBM sees each
 //     576-dim row once) with the transposing 64-bit LDS read.
+//
+// Given the split scorer's scores instead of a selection (the decode step),
+// every split block first selects its request's pages itself, with the exact
+// selection of the indexer kernels, in LDS that the tile buffer takes over
+// afterwards; split 0 writes the selection row.
 #include "vx_device.h"
 #include "vx_internal.h"
+#include "vx_select.h"
 
 namespace vx {
 namespace {
@@ -47,6 +53,13 @@ static_assert(kKS * 16 * 4 == kDqk, "k split");
 
 __device__ __forceinline__ float neg_inf() { return -INFINITY; }
 
+// Selection scratch inside the tile buffer: keys [round4(n)], list [k_tot],
+// then the histograms.
+__host__ __device__ constexpr size_t mla_select_offset(int score_stride, int k_tot) {
+  return (((size_t)round4(score_stride) + (size_t)k_tot) * 4 + 15) / 16 * 16;
+}
+
+template <bool SELECT>
 __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint8_t ktile[kT * kLdsRow];
   __shared__ __align__(16) float spart[4][64 * kPartStride];
@@ -63,7 +76,51 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + kPage - 1) / kPage;
   const int32_t* selrow = a.sel ? a.sel + (size_t)b * a.k_tot : nullptr;
-  if (w == 0) {
+  if constexpr (SELECT) {
+    // the request's pages from the indexer's scores (H_kv == 1)
+    uint32_t* keys = reinterpret_cast<uint32_t*>(ktile);
+    int32_t* list = reinterpret_cast<int32_t*>(keys + round4(a.score_stride));
+    SelectLds<kThreads>& sl =
+        *reinterpret_cast<SelectLds<kThreads>*>(ktile + mla_select_offset(a.score_stride, a.k_tot));
+    const int n_cand = max(n_b - a.n_bos - a.n_eos, 0);
+    select_init<kThreads>(sl);
+    __syncthreads();
+    if (n_cand > a.topk && a.topk > 0) {
+      const float* sc = a.scores + (size_t)b * a.score_stride;
+      constexpr int kIn = 8;
+      for (int i0 = tid; i0 < n_cand; i0 += kIn * kThreads) {
+        float v[kIn];
+#pragma unroll
+        for (int j = 0; j < kIn; ++j) v[j] = sc[min(i0 + j * kThreads, n_cand - 1)];
+#pragma unroll
+        for (int j = 0; j < kIn; ++j) {
+          const int i = i0 + j * kThreads;
+          if (i < n_cand) {
+            const uint32_t k = order_key(v[j]);
+            keys[i] = k;
+            select_count<kThreads>(sl, k);
+          }
+        }
+      }
+    }
+    const int count = select_pages<kThreads>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos,
+                                             a.k_tot, nullptr, list, sl);
+    __syncthreads();
+    if (split == 0) {
+      int32_t* srow = a.sel_out + (size_t)b * a.k_tot;
+      for (int i = tid; i < a.k_tot; i += kThreads) srow[i] = i < count ? list[i] : -1;
+    }
+    const int p0 = split * a.pages_per_split;
+    const int p1 = min(p0 + a.pages_per_split, count);
+    const int np = max(p1 - p0, 0);
+    const int32_t* ptb = a.pt + (size_t)b * a.pt_stride;
+    for (int i = tid; i < np; i += kThreads) {
+      const int logi = list[p0 + i];
+      page_logi[i] = logi;
+      page_phys[i] = ptb[logi];
+    }
+    if (tid == 0) s_count = count;
+  } else if (w == 0) {
     int count = n_b;
     if (selrow) {
       count = a.k_tot;
@@ -81,11 +138,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
   const int p0 = split * a.pages_per_split;
   const int p1 = min(p0 + a.pages_per_split, count);
   const int np = max(p1 - p0, 0);
-  const int32_t* ptb = a.pt + (size_t)b * a.pt_stride;
-  for (int i = tid; i < np; i += kThreads) {
-    const int logi = selrow ? selrow[p0 + i] : p0 + i;
-    page_logi[i] = logi;
-    page_phys[i] = ptb[logi];
+  if constexpr (!SELECT) {
+    const int32_t* ptb = a.pt + (size_t)b * a.pt_stride;
+    for (int i = tid; i < np; i += kThreads) {
+      const int logi = selrow ? selrow[p0 + i] : p0 + i;
+      page_logi[i] = logi;
+      page_phys[i] = ptb[logi];
+    }
   }
 
   // query slice as the B operand of S^T = K Q^T: head hl, dims 144w + 16ks + 8hh ..
@@ -258,10 +317,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
 
 int mla_max_pages_per_split() { return kMaxPages; }
 
+bool mla_select_fits(int score_stride, int k_tot) {
+  return mla_select_offset(score_stride, k_tot) + sizeof(SelectLds<kThreads>) <= sizeof(uint8_t) *
+                                                                                    kT * kLdsRow;
+}
+
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s) {
   if (a.pages_per_split > kMaxPages || a.S_p != kPage || a.H_kv != 1 || a.H_q > kHeads)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_mla_kernel, dim3(a.n_split, a.B), dim3(kThreads), 0, s, a);
+  if (a.scores) {
+    if (!mla_select_fits(a.score_stride, a.k_tot) || !a.sel_out) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mla_kernel<true>), dim3(a.n_split, a.B), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_mla_kernel<false>), dim3(a.n_split, a.B), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

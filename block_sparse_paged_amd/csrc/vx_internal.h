@@ -132,6 +132,9 @@ hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t
 // D = D_qk = D_v for this path; G = H_q / H_kv.
 hipError_t launch_decode_split(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
+// Whether the MLA decode can select its pages itself (scores given) for this
+// score row length and selection size.
+bool mla_select_fits(int score_stride, int k_tot);
 int mla_max_pages_per_split();
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
 bool decode_step_supported(int dtype, int D, int G);
