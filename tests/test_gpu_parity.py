@@ -656,3 +656,52 @@ def test_radix_topk_arguments(vx):
         with pytest.raises(vx.VxError) as e:
             vx.score_topk_radix(c.kv, bt, q, w.topk, w.n_bos, w.n_eos, levels, rnd, sel, ws)
         assert e.value.status == vx.VX_ERR_INVALID_ARGUMENT
+
+
+def test_selection_beyond_register_keys(vx):
+    """About 12,000 candidates per (request, KV head): more than 16 per
+    thread of a 512-thread block, so the selection reads its keys from LDS in
+    runs instead of holding them in registers.  Indexer and decode step both
+    match the oracle; the lossy radix call rejects the size."""
+    lens = (16 * 12001 + 5, 16 * 9000)
+    w = synth.Workload(name="many_cand", batch=len(lens), num_q_heads=4, num_kv_heads=2,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, dtype="bf16", topk=300,
+                       structure="page_offset", seed=86, seq_lens=lens, spare_pages=2)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    H.fix_gaps(c, range(w.batch))
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    sel2, out2, lse2 = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2)
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel2, out2, lse2)
+    bt = c.batch(vx)
+    rnd = torch.zeros(w.batch * w.num_kv_heads, dtype=torch.int32, device="cuda")
+    ws = vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, c.kv, bt)
+    with pytest.raises(vx.VxError) as e:
+        vx.score_topk_radix(c.kv, bt, q, w.topk, w.n_bos, w.n_eos, 1, rnd, sel, ws)
+    assert e.value.status == vx.VX_ERR_UNSUPPORTED
+
+
+def test_selection_beyond_register_keys_4_wave_blocks(vx):
+    """The same for the fused step's 4-wave blocks (512 or more units): two
+    requests with more than 16 candidates per thread of a 256-thread block
+    among 510 short ones."""
+    lens = (16 * 5000 + 3, 16 * 4500) + (17, 40, 1, 64, 33) * 102
+    w = synth.Workload(name="many_cand4", batch=len(lens), num_q_heads=2, num_kv_heads=1,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, dtype="bf16", topk=200,
+                       structure="page_offset", seed=87, seq_lens=lens, spare_pages=2)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    H.build_setup_centroids(vx, c)
+    reqs = [0, 1, 2, 5, 300, w.batch - 1]
+    H.fix_gaps(c, reqs)
+    q = c.q_host.cuda()
+    sel, out, lse = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, H.run_indexer(vx, c, q))
+    for b in reqs:
+        _check_request(vx, c, b, sel, out, lse)
