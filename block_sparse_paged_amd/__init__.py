@@ -240,6 +240,8 @@ def score_topk_radix(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bo
             rnd.dtype.is_floating_point:
         raise ValueError("rnd must be a contiguous 32-bit integer CUDA tensor")
     kvs, bs = kv.struct(), batch.struct()
+    if rnd.numel() < bs.batch * kvs.num_kv_heads:
+        raise ValueError("rnd needs one word per (request, KV head)")
     _check(load_library().vx_score_topk_radix(
         ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, levels, _ptr(rnd),
         _ptr(sel), _ptr(workspace), workspace.numel(), _stream(stream)), "vx_score_topk_radix")

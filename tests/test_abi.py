@@ -235,3 +235,36 @@ def test_split_override_changes_plan(lib):
         assert n2 == 0                                      # one split: direct output
     finally:
         lib.vx_set_pages_per_split(0)
+
+
+def test_radix_and_append_arguments_rejected(lib):
+    r = ctypes.byref
+    kv, bt = kv_struct(), batch_struct()
+    radix = lib.vx_score_topk_radix
+    for levels in (0, 3, -1):
+        assert radix(r(kv), r(bt), FAKE, 30, 1, 1, levels, FAKE, FAKE, FAKE, 1 << 30,
+                     None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert radix(r(kv), r(bt), FAKE, 30, 1, 1, 1, None, FAKE, FAKE, 1 << 30,
+                 None) == vx.VX_ERR_INVALID_ARGUMENT                  # no random words
+    big = batch_struct(max_pages_per_req=9000, max_seq_len=9000 * 16)
+    assert radix(r(kv), r(big), FAKE, 30, 1, 1, 2, FAKE, FAKE, FAKE, 1 << 30,
+                 None) == vx.VX_ERR_UNSUPPORTED                       # > 8192 candidates
+    assert radix(r(kv), r(batch_struct(batch=0)), None, 30, 1, 1, 1, None, None, None, 0,
+                 None) == vx.VX_OK
+    app = lib.vx_append_kv
+    for k_src, v_src, rows, max_new, upd in ((None, FAKE, 8, 1, 1), (FAKE, None, 8, 1, 1),
+                                             (FAKE, FAKE, -1, 1, 1), (FAKE, FAKE, 8, -1, 1),
+                                             (FAKE, FAKE, 8, 1, 2)):
+        assert app(r(kv), r(bt), k_src, v_src, FAKE, FAKE, rows, max_new, upd,
+                   None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert app(r(kv), r(bt), FAKE, FAKE, None, FAKE, 8, 1, 1, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert app(r(kv_struct(centroids=None)), r(bt), FAKE, FAKE, FAKE, FAKE, 8, 1, 1,
+               None) == vx.VX_ERR_INVALID_ARGUMENT                    # centroids to update
+    mla = kv_struct(head_dim_qk=576, head_dim_v=512, num_kv_heads=1, page_size=64,
+                    v_aliases_k=1, v_cache=None)
+    mbt = batch_struct(num_q_heads=32, max_seq_len=64 * 64)
+    assert app(r(mla), r(mbt), FAKE, FAKE, FAKE, FAKE, 8, 1, 1,
+               None) == vx.VX_ERR_INVALID_ARGUMENT                    # V is part of K
+    assert app(r(kv), r(bt), FAKE, FAKE, FAKE, FAKE, 8, 0, 1, None) == vx.VX_OK      # nothing new
+    assert app(r(kv), r(batch_struct(batch=0)), None, None, None, None, 0, 5, 1,
+               None) == vx.VX_OK
