@@ -33,7 +33,7 @@ namespace {
 constexpr int kScoreThreads = 512;
 constexpr int kTopkThreads = 512;
 constexpr int kFusedThreads = 512;
-constexpr int kLoadsInFlight = 16;   // wave-loads issued before the first is used
+constexpr int kSplitLoads = 8;      // wave-loads in flight per lane in the split scorer
 // (KV head, segment, row group) triples of a completed page one scoring
 // block takes at most (two per thread)
 constexpr int kScoreCentroidPairs = 2 * kScoreThreads;
@@ -70,22 +70,28 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs 
 }
 
 // ---------------------------------------------------------------- split
+// Order of a scoring block, so that HBM is busy as early as possible: the
+// query rows, the block's page-table slice and the request length are
+// loaded together; once the page ids are in LDS the first centroid loads
+// are issued, and only then are the group-mean queries formed (their loads
+// have long arrived) and the completed page's rows requested.
 template <typename T, int D>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   using V = Vec16<T>;
   constexpr int E = V::E;
   constexpr int LH = D / E;                 // 16-byte segments per centroid row
-  constexpr int U = kLoadsInFlight;
   extern __shared__ float smem[];           // qbar [H_kv][D] then phys ids
   float* qbar = smem;
   int32_t* phys = reinterpret_cast<int32_t*>(smem + a.H_kv * D);
 
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // group-mean query of every KV head, fp32: thread (chunk, head, segment)
   // sums eight query heads in order, the chunks' partials are then added in
-  // chunk order.  The first item's query loads and the first page-table
-  // entry are issued before the request length is known.
+  // chunk order.  Every load up to the first centroid batch is issued by
+  // every thread (indices clamped, surplus values unused), so that the waits
+  // for the query rows count the centroid loads behind them exactly.
   const int G = a.H_q / a.H_kv;
   const int NCH = (G + 7) / 8;
   const int QS = a.H_kv * LH;                 // (head, segment) pairs
@@ -93,11 +99,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const float invG = 1.0f / (float)G;
   float* qpart = reinterpret_cast<float*>(phys + a.cand_per_block);   // [NCH][H_kv * D] when NCH > 1
   auto q_load = [&](int i, uint4* v) {
+    i = min(i, QS * NCH - 1);
     const int ch = i / QS, hs = i - ch * QS;
     const int h = hs / LH, sg = hs - h * LH;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (ch * 8 + j < G) v[j] = ld16(qb + (size_t)(h * G + ch * 8 + j) * D + sg * E);
+    for (int j = 0; j < 8; ++j) v[j] = ld16(qb + (size_t)(h * G + min(ch * 8 + j, G - 1)) * D + sg * E);
   };
   auto q_store = [&](int i, const uint4* v) {
     const int ch = i / QS, hs = i - ch * QS;
@@ -119,28 +125,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     for (int e = 0; e < E; ++e) dst[h * D + sg * E + e] = NCH == 1 ? acc[e] * invG : acc[e];
   };
   uint4 qv[8];
-  if (tid < QS * NCH) q_load(tid, qv);
+  q_load(tid, qv);
   const int32_t* ptb = a.pt + (size_t)b * a.pt_stride + a.n_bos;
   const int c0 = blockIdx.x * a.cand_per_block;
-  const int pv = tid < a.cand_per_block && c0 + tid < a.score_stride - a.n_bos ? ptb[c0 + tid] : 0;
+  const int pv = ptb[max(min(c0 + tid, a.score_stride - a.n_bos - 1), 0)];   // used for tid < nc
 
   int seq = a.seq_lens[b];
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
   const int n_cand = n_b - a.n_bos - a.n_eos;
   // the completed page's centroid rows, shared by the request's blocks by
-  // (KV head, segment) units: rows loaded now, summed after the scoring
+  // (KV head, segment) units: page id now, rows once the scoring loads are
+  // issued, sums after the scoring
   using SC = SegmentCentroid<T, D, kScoreThreads, kScoreCentroidPairs / kScoreThreads>;
   const int n_units = a.H_kv * SC::S::SEGS;
   const int u0 = (int)((long long)blockIdx.x * n_units / gridDim.x);
   const int nu = (int)((long long)(blockIdx.x + 1) * n_units / gridDim.x) - u0;
   const bool upd = a.update_completed && nu > 0 && seq > 0 && seq % a.S_p == 0;
+  const int cpage = upd ? a.pt[(size_t)b * a.pt_stride + n_b - 1] : 0;
   SC sc;
-  int cpage = 0;
-  if (upd) {
-    cpage = a.pt[(size_t)b * a.pt_stride + n_b - 1];
-    sc.load(reinterpret_cast<const T*>(a.k) + (size_t)cpage * a.H_kv * a.S_p * D, a.S_p, u0, nu);
-  }
+  auto centroid_load = [&]() {
+    if (upd)
+      sc.load(reinterpret_cast<const T*>(a.k) + (size_t)cpage * a.H_kv * a.S_p * D, a.S_p, u0, nu);
+  };
   float* cred = smem + a.H_kv * D + a.cand_per_block + (NCH > 1 ? NCH * a.H_kv * D : 0);
   auto centroid_done = [&]() {
     if (!upd) return;
@@ -150,77 +157,110 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       SC::finish(cred, a.S_p, reinterpret_cast<T*>(a.cent_out) + (size_t)cpage * a.H_kv * D, u0, tid);
   };
   if (c0 >= n_cand) {
+    centroid_load();
     centroid_done();
     return;
   }
   const int c1 = min(c0 + a.cand_per_block, n_cand);
   const int nc = c1 - c0;
-
-  if (tid < QS * NCH) q_store(tid, qv);
-  for (int i = tid + kScoreThreads; i < QS * NCH; i += kScoreThreads) {
-    q_load(i, qv);
-    q_store(i, qv);
-  }
-  if (NCH > 1) {
-    __syncthreads();
-    for (int i = tid; i < a.H_kv * D; i += kScoreThreads) {
-      float x = 0.f;
-      for (int ch = 0; ch < NCH; ++ch) x += qpart[(size_t)ch * a.H_kv * D + i];
-      qbar[i] = x * invG;
-    }
-  }
   if (tid < nc) phys[tid] = pv;
   for (int i = tid + kScoreThreads; i < nc; i += kScoreThreads) phys[i] = ptb[c0 + i];
   __syncthreads();
 
-  const int wave = tid >> 6, lane = tid & 63;
+  // group-mean queries into qbar (every query load was issued first)
+  auto q_finish = [&]() {
+    if (tid < QS * NCH) q_store(tid, qv);
+    for (int i = tid + kScoreThreads; i < QS * NCH; i += kScoreThreads) {
+      q_load(i, qv);
+      q_store(i, qv);
+    }
+    if (NCH > 1) {
+      __syncthreads();
+      for (int i = tid; i < a.H_kv * D; i += kScoreThreads) {
+        float x = 0.f;
+        for (int ch = 0; ch < NCH; ++ch) x += qpart[(size_t)ch * a.H_kv * D + i];
+        qbar[i] = x * invG;
+      }
+    }
+    __syncthreads();
+  };
+
   const T* cent = reinterpret_cast<const T*>(a.cent);
   float* out = a.scores + (size_t)b * a.H_kv * a.score_stride;
   const int rows = nc * a.H_kv;
 
   if constexpr (LH <= 64) {
+    // Rows r = c * H_kv + h (the H_kv rows of a page are contiguous), R per
+    // wave-load, lane group grp taking rows wave * R + grp + STEP * j.  A
+    // wave's rows come in batches of U wave-loads; load u of the next batch
+    // is issued as soon as load u of this batch is consumed, so U loads stay
+    // in flight per lane through the whole scoring (past the last row the
+    // index is clamped to it: the surplus loads of the last batch hit the
+    // cache).  Each lane keeps the sums of its group's loads seg, seg + LH,
+    // ... and stores them after the batch.
     constexpr int R = 64 / LH;              // rows per wave-load
     constexpr int STEP = (kScoreThreads / 64) * R;   // rows per block-wide wave-load
+    constexpr int U = kSplitLoads;
+    constexpr int NS = (U + LH - 1) / LH;   // sums a lane stores per batch
     const int seg = lane % LH, grp = lane / LH;
+    const int rw = wave * R + grp;          // this lane's first row
+    const int nbat = rows > wave * R ? (rows - wave * R + STEP * U - 1) / (STEP * U) : 0;
+    auto row_off = [&](int r) -> size_t {
+      const int rc = min(r, rows - 1);
+      const int c = rc / a.H_kv, h = rc - c * a.H_kv;
+      return ((size_t)phys[c] * a.H_kv + h) * D + seg * E;
+    };
+    const T* cs = cent;
+    uint4 buf[U];
+    if (nbat > 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) buf[u] = ld16(cs + row_off(rw + u * STEP));
+    }
+    q_finish();
+    centroid_load();
     // with H_kv dividing STEP every row a lane touches has the same KV head,
     // so that head's query segment stays in registers
     const bool fixed_head = STEP % a.H_kv == 0;
     float qr[E];
     {
-      const int h0 = (wave * R + grp) % a.H_kv;
+      const int h0 = rw % a.H_kv;
 #pragma unroll
       for (int e = 0; e < E; ++e) qr[e] = qbar[h0 * D + seg * E + e];
     }
-    for (int r0 = wave * R; r0 < rows; r0 += STEP * U) {
-      uint4 buf[U];
+    for (int k = 0; k < nbat; ++k) {
+      const int r0 = rw + k * STEP * U;     // this lane's row of load 0
+      size_t nx[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) nx[u] = row_off(r0 + STEP * U + u * STEP);
+      float mine[NS];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * STEP + grp;
-        if (r < rows) {
-          const int c = r / a.H_kv, h = r - c * a.H_kv;
-          buf[u] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + seg * E);
-        } else {
-          buf[u] = make_uint4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * STEP + grp;
-        const int rc = r < rows ? r : 0;
-        const int c = rc / a.H_kv, h = rc - c * a.H_kv;
+        const int r = r0 + u * STEP;
         float f[E];
         V::unpack(buf[u], f);
+        buf[u] = ld16(cs + nx[u]);
         float acc = 0.f;
         if (fixed_head) {
 #pragma unroll
           for (int e = 0; e < E; ++e) acc = fmaf(qr[e], f[e], acc);
         } else {
+          const int rc = r < rows ? r : 0;
+          const int h = rc - (rc / a.H_kv) * a.H_kv;
           const float* qh = qbar + h * D + seg * E;
 #pragma unroll
           for (int e = 0; e < E; ++e) acc = fmaf(qh[e], f[e], acc);
         }
         acc = lane_group_sum<LH>(acc);
-        if (seg == 0 && r < rows) out[(size_t)h * a.score_stride + c0 + c] = acc;
+        if (seg == u % LH) mine[u / LH] = acc;
+      }
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int u = seg + j * LH;
+        const int r = r0 + u * STEP;
+        if (u < U && r < rows) {
+          const int c = r / a.H_kv, h = r - c * a.H_kv;
+          out[(size_t)h * a.score_stride + c0 + c] = mine[j];
+        }
       }
     }
   } else {
@@ -231,25 +271,26 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     constexpr int TL = LH - 64;             // tail segments per row (8)
     constexpr int RT = 64 / TL;             // rows per tile (8)
     struct Tile { uint4 hb[RT]; uint4 tb; };
-    auto issue = [&](int r0, Tile& tl) {
+    auto issue = [&](int r0, Tile& tl) {     // rows past the last are clamped to it
 #pragma unroll
       for (int i = 0; i < RT; ++i) {
-        const int r = r0 + i;
-        if (r < rows) {
-          const int c = r / a.H_kv, h = r - c * a.H_kv;
-          tl.hb[i] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + lane * E);
-        } else {
-          tl.hb[i] = make_uint4(0, 0, 0, 0);
-        }
+        const int r = min(r0 + i, rows - 1);
+        const int c = r / a.H_kv, h = r - c * a.H_kv;
+        tl.hb[i] = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + lane * E);
       }
-      const int tr = r0 + lane / TL, tseg = 64 + lane % TL;
-      if (tr < rows) {
-        const int c = tr / a.H_kv, h = tr - c * a.H_kv;
-        tl.tb = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + tseg * E);
-      } else {
-        tl.tb = make_uint4(0, 0, 0, 0);
-      }
+      const int tr = min(r0 + lane / TL, rows - 1), tseg = 64 + lane % TL;
+      const int c = tr / a.H_kv, h = tr - c * a.H_kv;
+      tl.tb = ld16(cent + ((size_t)phys[c] * a.H_kv + h) * D + tseg * E);
     };
+    // eight rows per tile, two tiles in flight per wave, both issued before
+    // the queries are formed
+    constexpr int NW = kScoreThreads / 64;
+    Tile ta, tb;
+    int r0 = wave * RT;
+    if (r0 < rows) issue(r0, ta);
+    if (r0 + NW * RT < rows) issue(r0 + NW * RT, tb);
+    q_finish();
+    centroid_load();
     // with one KV head (MLA) the query segments a lane needs stay in registers
     const bool one_head = a.H_kv == 1;
     float qh1[E], qt1[E];
@@ -288,17 +329,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         if (lane == 0 && r < rows) out[(size_t)h * a.score_stride + c0 + c] = acc;
       }
     };
-    // eight rows per tile, two tiles in flight per wave
-    constexpr int NW = kScoreThreads / 64;
-    Tile ta, tb;
-    int r0 = wave * RT;
-    if (r0 < rows) issue(r0, ta);
     for (; r0 < rows; r0 += 2 * NW * RT) {
-      const int r1 = r0 + NW * RT, r2 = r1 + NW * RT;
-      if (r1 < rows) issue(r1, tb);
+      const int r1 = r0 + NW * RT, r2 = r1 + NW * RT, r3 = r2 + NW * RT;
       consume(r0, ta);
       if (r2 < rows) issue(r2, ta);
       if (r1 < rows) consume(r1, tb);
+      if (r3 < rows) issue(r3, tb);
     }
   }
   centroid_done();
