@@ -179,6 +179,66 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   if (tid == 0 && a.lse) a.lse[row] = tot > 0.f ? (mx + __log2f(tot)) * kLn2 : -INFINITY;
 }
 
+// K5 for few splits (the sparse paths' usual case): one wave per row, so no
+// block-wide reductions.  Lane i holds split i's (m, l); every partial-o load
+// is issued before the weights are known.  A split with an empty page range
+// has l = 0 and weight 0, and its slots are never folded in (not even
+// multiplied by zero), so whatever they hold is ignored.  The maximum, the
+// weights, their sum and the accumulation order are those of combine_kernel.
+constexpr int kCombineFew = 8;
+
+template <typename T, int DV>
+__global__ __launch_bounds__(64) void combine_few_kernel(CombineArgs a) {
+  constexpr int PD = DV / 64;               // output dims per lane
+  static_assert(PD * 64 == DV, "rows of a multiple of 64 dims");
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;            // b * H_q + hq
+  const int n = a.n_split;
+  const float2 mli = *reinterpret_cast<const float2*>(a.part_ml + (row * n + min(lane, n - 1)) * 2);
+  const float* po = a.part_o + row * n * DV + lane * PD;
+  float x[kCombineFew][PD];
+#pragma unroll
+  for (int i = 0; i < kCombineFew; ++i) {
+    if (i < n) {
+      const float* p = po + (size_t)i * DV;
+      if constexpr (PD % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < PD; j += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(p + j);
+          x[i][j] = v.x; x[i][j + 1] = v.y; x[i][j + 2] = v.z; x[i][j + 3] = v.w;
+        }
+      } else if constexpr (PD == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        x[i][0] = v.x; x[i][1] = v.y;
+      } else {
+        x[i][0] = p[0];
+      }
+    }
+  }
+  const bool valid = lane < n && mli.y > 0.f;
+  const float mx = wave_max(valid ? mli.x : -INFINITY);
+  const float wl = valid ? exp2f(mli.x - mx) : 0.f;
+  const float tot = wave_sum(lane < n ? wl * mli.y : 0.f);
+  float acc[PD];
+#pragma unroll
+  for (int j = 0; j < PD; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCombineFew; ++i) {
+    if (i < n) {
+      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+      if (wi != 0.f) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) acc[j] = fmaf(wi, x[i][j], acc[j]);
+      }
+    }
+  }
+  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+  T* op = reinterpret_cast<T*>(a.out) + row * DV + lane * PD;
+#pragma unroll
+  for (int j = 0; j < PD; ++j) op[j] = Vec16<T>::from_f32(acc[j] * inv);
+  if (lane == 0 && a.lse) a.lse[row] = tot > 0.f ? (mx + __log2f(tot)) * kLn2 : -INFINITY;
+}
+
 template <typename T, int D, int G>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
   constexpr int HS = attend_head_slices<G>(), PF = attend_prefetch<T, D>();
@@ -205,7 +265,10 @@ hipError_t run_decode_g(int G, const DecodeArgs& a, hipStream_t s) {
 
 template <typename T, int DV>
 hipError_t run_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<T, DV>), dim3(a.B * a.H_q), dim3(kCombineThreads), 0, s, a);
+  if (a.n_split <= kCombineFew)
+    hipLaunchKernelGGL((combine_few_kernel<T, DV>), dim3(a.B * a.H_q), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, DV>), dim3(a.B * a.H_q), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -15,15 +15,17 @@
 // split   K2 score_kernel: blocks over (candidate chunk, request) score all
 //         KV heads of their pages (the H_kv rows of a page are contiguous, so
 //         a wave-load reads 1 KiB of consecutive heads) into the workspace;
-//         K3 topk_kernel: one block per (request, KV head) selects.  Used when
+//         K3 topk_kernel: one block per (request, KV head) selects (in the
+//         decode step the split decode kernels select instead).  Used when
 //         few (request, KV head) units exist (long contexts, MLA's single
 //         latent head).
 //
-// Selection (both schedules): the k-th largest (key, page) pair from a
-// histogram of the key range in at most 1024 bins (every wave locating the
-// boundary bin itself), the boundary bin's keys ranked exactly (or the bin
-// histogrammed again when it holds more than 256), then the union with the
-// reserved pages compacted in ascending page order with one block-wide scan.
+// Selection (both schedules, vx_select.h): the k-th largest (key, page) pair
+// from histograms of the key range in at most 1024 bins, each level
+// narrowing the boundary bin's range by ten bits until that bin is taken
+// whole (every wave locating the boundary bin itself), then the union with
+// the reserved pages compacted in ascending page order with one block-wide
+// scan.
 #include "vx_centroid.h"
 #include "vx_select.h"
 
