@@ -29,12 +29,13 @@ VX_ERR_HIP = 4
 
 VX_F32, VX_BF16 = 0, 1
 VX_OP_SCORE_TOPK, VX_OP_SPARSE_DECODE, VX_OP_FULL_DECODE, VX_OP_DECODE_STEP = 0, 1, 2, 3
+VX_OP_DECODE_LAYERS = 4
 
 # Symbols include/vx.h declares (checked by the ABI tests).
 EXPORTS = ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
            "vx_sparse_paged_decode",
-           "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
-           "vx_set_pages_per_split", "vx_status_string", "vx_version")
+           "vx_full_paged_decode", "vx_sparse_decode_step", "vx_decode_layers",
+           "vx_workspace_size", "vx_set_pages_per_split", "vx_status_string", "vx_version")
 
 
 class VxError(RuntimeError):
@@ -85,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_full_paged_decode.argtypes = [kvp, btp, VP, F32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_decode_step.argtypes = [kvp, btp, VP, I32, I32, I32, I32, F32, VP, VP, VP,
                                           VP, SZ, VP]
+    lib.vx_decode_layers.argtypes = [kvp, btp, VP, I32, VP, I32, I32, I32, I32, F32, VP, VP, VP,
+                                     VP, SZ, VP]
     lib.vx_workspace_size.argtypes = [I32, kvp, btp, I32, P(SZ)]
     lib.vx_set_pages_per_split.argtypes = [I32]
     lib.vx_status_string.argtypes = [I32]
@@ -92,8 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_version.argtypes = []
     for name in ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
                  "vx_sparse_paged_decode",
-                 "vx_full_paged_decode", "vx_sparse_decode_step", "vx_workspace_size",
-                 "vx_set_pages_per_split", "vx_version"):
+                 "vx_full_paged_decode", "vx_sparse_decode_step", "vx_decode_layers",
+                 "vx_workspace_size", "vx_set_pages_per_split", "vx_version"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -378,3 +381,64 @@ def prepare_sparse_decode_step(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos,
             _ptr(workspace), workspace.numel(), _stream(stream))
     return PreparedCall(lib.vx_sparse_decode_step, args, "vx_sparse_decode_step",
                         (kvs, bs, kv, batch, q, sel, out, lse, workspace))
+
+
+def prepare_decode_layers(kvs: list, batch: Batch, qs: list, dense: Optional[list], topk: int,
+                          n_bos: int, n_eos: int, update_completed: bool, sm_scale: float,
+                          sels: Optional[list], outs: list, lses: Optional[list],
+                          workspace: torch.Tensor, stream=None) -> PreparedCall:
+    """vx_decode_layers over len(kvs) layers: layer l runs full attention
+    when dense[l] is true, else the fused sparse step into sels[l].  The
+    host arrays of structs and pointers are built here, once."""
+    n = len(kvs)
+    if len(qs) != n or len(outs) != n or (dense is not None and len(dense) != n) or \
+            (sels is not None and len(sels) != n) or (lses is not None and len(lses) != n):
+        raise ValueError("one entry per layer in every list")
+    for t in list(qs) + list(outs):
+        _need(t, "q/out")
+    for t in (sels or []):
+        if t is not None:
+            _need(t, "sel", torch.int32)
+    kv_arr = (PagedKVStruct * max(n, 1))(*[kv.struct() for kv in kvs])
+    bs = batch.struct()
+    VPA = ctypes.c_void_p * max(n, 1)
+    q_arr = VPA(*[t.data_ptr() for t in qs])
+    out_arr = VPA(*[t.data_ptr() for t in outs])
+    sel_arr = None if sels is None else VPA(*[0 if t is None else t.data_ptr() for t in sels])
+    lse_arr = None if lses is None else VPA(*[0 if t is None else t.data_ptr() for t in lses])
+    dense_arr = None if dense is None else (ctypes.c_uint8 * max(n, 1))(*[1 if d else 0 for d in dense])
+    lib = load_library()
+    args = (kv_arr, ctypes.byref(bs), q_arr, n, dense_arr, topk, n_bos, n_eos,
+            1 if update_completed else 0, float(sm_scale), sel_arr, out_arr, lse_arr,
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall(lib.vx_decode_layers, args, "vx_decode_layers",
+                        (kv_arr, bs, q_arr, out_arr, sel_arr, lse_arr, dense_arr, list(kvs), batch,
+                         list(qs), list(outs), list(sels or []), list(lses or []), workspace))
+
+
+def decode_layers(kvs: list, batch: Batch, qs: list, dense: Optional[list], topk: int,
+                  n_bos: int, n_eos: int, update_completed: bool, sm_scale: float,
+                  sels: Optional[list], outs: list, lses: Optional[list],
+                  workspace: torch.Tensor, stream=None):
+    """vx_decode_layers: one decode step through several attention layers."""
+    prepare_decode_layers(kvs, batch, qs, dense, topk, n_bos, n_eos, update_completed, sm_scale,
+                          sels, outs, lses, workspace, stream)()
+
+
+def capture_graph(make_call) -> "torch.cuda.CUDAGraph":
+    """Capture the libvx launches of ``make_call(stream)()`` into a graph.
+
+    ``make_call`` receives the capturing stream and returns a prepared call
+    (for instance ``lambda s: prepare_decode_layers(..., stream=s)``); the
+    call is made once on a side stream first, so that every one-time host
+    query happens outside the capture.  Replaying the graph repeats the
+    launches with the pointers, lengths bound and plan of the capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        make_call(side)()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        make_call(torch.cuda.current_stream())()
+    return g

@@ -410,6 +410,59 @@ size_t step_lds_bytes(int max_pages, int k_tot, int D, int G, int ordered_batch)
   return dyn + stat;
 }
 
+// Host-side validation of vx_full_paged_decode / vx_sparse_decode_step
+// (everything those calls check before their first HIP call).
+vx_status full_decode_check(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                            float sm_scale, const void* out, const void* workspace,
+                            size_t workspace_bytes) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) || !batch->page_table ||
+      !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  const DecodePlan p = plan_decode(kv, batch, max_pages_eff(kv, batch), false);
+  if (workspace_bytes < p.ws_bytes()) return VX_ERR_WORKSPACE_TOO_SMALL;
+  if (p.ws_bytes() > 0 && !workspace) return VX_ERR_INVALID_ARGUMENT;
+  return VX_OK;
+}
+
+vx_status step_check(const vx_paged_kv* kv, const vx_batch* batch, const void* q, int32_t topk,
+                     int32_t n_bos, int32_t n_eos, int32_t update_completed, float sm_scale,
+                     const int32_t* sel, const void* out, const void* workspace,
+                     size_t workspace_bytes) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (topk < 0 || n_bos < 0 || n_eos < 1) return VX_ERR_INVALID_ARGUMENT;
+  if ((long long)topk + n_bos + n_eos > 0x7fffffffLL) return VX_ERR_INVALID_ARGUMENT;
+  if (update_completed != 0 && update_completed != 1) return VX_ERR_INVALID_ARGUMENT;
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !sel || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) ||
+      !kv->centroids || !batch->page_table || !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  if (max_pages_eff(kv, batch) > kMaxCandidates) return VX_ERR_UNSUPPORTED;
+  if (workspace_bytes < step_ws_bytes(kv, batch, topk + n_bos + n_eos))
+    return VX_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return VX_ERR_INVALID_ARGUMENT;
+  return VX_OK;
+}
+
+// Workspace of vx_decode_layers: the larger of a step's and a dense call's.
+size_t layers_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
+  return std::max(step_ws_bytes(kv, bt, k_tot),
+                  plan_decode(kv, bt, max_pages_eff(kv, bt), false).ws_bytes());
+}
+
+bool same_shape(const vx_paged_kv& a, const vx_paged_kv& b) {
+  return a.dtype == b.dtype && a.page_size == b.page_size && a.num_kv_heads == b.num_kv_heads &&
+         a.head_dim_qk == b.head_dim_qk && a.head_dim_v == b.head_dim_v &&
+         a.v_aliases_k == b.v_aliases_k;
+}
+
 }  // namespace
 
 extern "C" {
@@ -516,14 +569,8 @@ vx_status vx_sparse_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, c
 vx_status vx_full_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                                float sm_scale, void* out, float* lse, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  vx_status st = check_kv(kv);
-  if (st != VX_OK) return st;
-  if ((st = check_batch(kv, batch)) != VX_OK) return st;
-  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
-  if (batch->batch == 0) return VX_OK;
-  if (!q || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) || !batch->page_table ||
-      !batch->seq_lens)
-    return VX_ERR_INVALID_ARGUMENT;
+  const vx_status st = full_decode_check(kv, batch, q, sm_scale, out, workspace, workspace_bytes);
+  if (st != VX_OK || batch->batch == 0) return st;
   return run_decode(kv, batch, q, nullptr, 0, sm_scale, out, lse, workspace, workspace_bytes,
                     stream);
 }
@@ -533,22 +580,11 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
                                 int32_t update_completed, float sm_scale, int32_t* sel,
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-  vx_status st = check_kv(kv);
-  if (st != VX_OK) return st;
-  if ((st = check_batch(kv, batch)) != VX_OK) return st;
-  if (topk < 0 || n_bos < 0 || n_eos < 1) return VX_ERR_INVALID_ARGUMENT;
-  if ((long long)topk + n_bos + n_eos > 0x7fffffffLL) return VX_ERR_INVALID_ARGUMENT;
-  if (update_completed != 0 && update_completed != 1) return VX_ERR_INVALID_ARGUMENT;
-  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
-  if (batch->batch == 0) return VX_OK;
-  if (!q || !sel || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) ||
-      !kv->centroids || !batch->page_table || !batch->seq_lens)
-    return VX_ERR_INVALID_ARGUMENT;
+  vx_status st = step_check(kv, batch, q, topk, n_bos, n_eos, update_completed, sm_scale, sel,
+                            out, workspace, workspace_bytes);
+  if (st != VX_OK || batch->batch == 0) return st;
   const int mp = max_pages_eff(kv, batch);
-  if (mp > kMaxCandidates) return VX_ERR_UNSUPPORTED;
   const int k_tot = topk + n_bos + n_eos;
-  if (workspace_bytes < step_ws_bytes(kv, batch, k_tot)) return VX_ERR_WORKSPACE_TOO_SMALL;
-  if (!workspace) return VX_ERR_INVALID_ARGUMENT;
   const int G = batch->num_q_heads / kv->num_kv_heads;
   const long long units = (long long)batch->batch * kv->num_kv_heads;
 
@@ -639,6 +675,42 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
                     stream);
 }
 
+vx_status vx_decode_layers(const vx_paged_kv* kv, const vx_batch* batch, const void* const* q,
+                           int32_t n_layers, const uint8_t* dense, int32_t topk, int32_t n_bos,
+                           int32_t n_eos, int32_t update_completed, float sm_scale,
+                           int32_t* const* sel, void* const* out, float* const* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n_layers < 0) return VX_ERR_INVALID_ARGUMENT;
+  if (n_layers == 0) return VX_OK;
+  if (!kv || !q || !out) return VX_ERR_INVALID_ARGUMENT;
+  // every layer is checked before the first launch
+  for (int l = 0; l < n_layers; ++l) {
+    if (!same_shape(kv[l], kv[0])) return VX_ERR_INVALID_ARGUMENT;
+    const bool is_dense = dense && dense[l];
+    vx_status st;
+    if (is_dense) {
+      st = full_decode_check(&kv[l], batch, q[l], sm_scale, out[l], workspace, workspace_bytes);
+    } else {
+      if (!sel) return VX_ERR_INVALID_ARGUMENT;
+      st = step_check(&kv[l], batch, q[l], topk, n_bos, n_eos, update_completed, sm_scale, sel[l],
+                      out[l], workspace, workspace_bytes);
+    }
+    if (st != VX_OK) return st;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    float* lse_l = lse ? lse[l] : nullptr;
+    const vx_status st =
+        dense && dense[l]
+            ? vx_full_paged_decode(&kv[l], batch, q[l], sm_scale, out[l], lse_l, workspace,
+                                   workspace_bytes, stream)
+            : vx_sparse_decode_step(&kv[l], batch, q[l], topk, n_bos, n_eos, update_completed,
+                                    sm_scale, sel[l], out[l], lse_l, workspace, workspace_bytes,
+                                    stream);
+    if (st != VX_OK) return st;
+  }
+  return VX_OK;
+}
+
 vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* batch,
                             int32_t k_tot, size_t* bytes) {
   if (!bytes) return VX_ERR_INVALID_ARGUMENT;
@@ -661,6 +733,11 @@ vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* b
       if (max_pages_eff(kv, batch) > kMaxCandidates) return VX_ERR_UNSUPPORTED;
       if (k_tot < 1) return VX_ERR_INVALID_ARGUMENT;
       *bytes = step_ws_bytes(kv, batch, k_tot);
+      return VX_OK;
+    case VX_OP_DECODE_LAYERS:
+      if (max_pages_eff(kv, batch) > kMaxCandidates) return VX_ERR_UNSUPPORTED;
+      if (k_tot < 1) return VX_ERR_INVALID_ARGUMENT;
+      *bytes = layers_ws_bytes(kv, batch, k_tot);
       return VX_OK;
   }
   return VX_ERR_INVALID_ARGUMENT;

@@ -79,7 +79,8 @@ typedef enum {
   VX_OP_SCORE_TOPK = 0,
   VX_OP_SPARSE_DECODE = 1,
   VX_OP_FULL_DECODE = 2,
-  VX_OP_DECODE_STEP = 3
+  VX_OP_DECODE_STEP = 3,
+  VX_OP_DECODE_LAYERS = 4
 } vx_op;
 
 /* The paged KV cache and its named centroid cache (the per-page summary
@@ -261,9 +262,41 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* The attention layers of one decode step in one call (README, "Using
+ * Your Sparse Attention with SGLang": with sparsity on, the layers listed as
+ * skipped run full attention; the serving setting replays the step as a
+ * captured graph).  For l = 0 .. n_layers-1, in order on `stream`:
+ *   dense && dense[l]:  vx_full_paged_decode(&kv[l], batch, q[l], sm_scale,
+ *                                            out[l], lse ? lse[l] : NULL, ...)
+ *   otherwise:          vx_sparse_decode_step(&kv[l], batch, q[l], topk, n_bos,
+ *                                             n_eos, update_completed, sm_scale,
+ *                                             sel[l], out[l], lse ? lse[l] : NULL, ...)
+ * Every layer shares `batch` (the same requests, page table and lengths) and
+ * the shapes of kv[0] (dtype, page size, heads and head dims; each layer has
+ * its own pools and centroid table), so every layer gets the same launch
+ * plan; one workspace serves all of them, one layer after the other.
+ *   kv         host array [n_layers] of caches
+ *   q, out     host arrays [n_layers] of device pointers, as in the calls above
+ *   dense      host uint8 [n_layers] (nonzero: full attention), or NULL (none)
+ *   sel        host array [n_layers] of device pointers; entries of dense
+ *              layers are not read (sel may be NULL when every layer is dense)
+ *   lse        host array [n_layers] of device pointers (entries may be NULL),
+ *              or NULL
+ *   workspace  at least vx_workspace_size(VX_OP_DECODE_LAYERS, ..., k_tot) bytes
+ * Every layer's arguments are checked before anything is launched.  No call
+ * in it synchronises, allocates or clears memory with a memset, so the whole
+ * call can be captured into a HIP graph and replayed (the graph then keeps
+ * the device pointers, lengths bound and plan of the capture). */
+vx_status vx_decode_layers(const vx_paged_kv* kv, const vx_batch* batch, const void* const* q,
+                           int32_t n_layers, const uint8_t* dense, int32_t topk, int32_t n_bos,
+                           int32_t n_eos, int32_t update_completed, float sm_scale,
+                           int32_t* const* sel, void* const* out, float* const* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes the call `op` needs for these shapes (k_tot is read for
- * VX_OP_SPARSE_DECODE and VX_OP_DECODE_STEP only).  Host-only; never touches the GPU.  The size
- * depends on the shapes and on the split override, nothing else. */
+ * VX_OP_SPARSE_DECODE, VX_OP_DECODE_STEP and VX_OP_DECODE_LAYERS only).
+ * Host-only; never touches the GPU.  The size depends on the shapes and on
+ * the split override, nothing else. */
 vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* batch,
                             int32_t k_tot, size_t* bytes /* host */);
 

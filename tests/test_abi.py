@@ -268,3 +268,48 @@ def test_radix_and_append_arguments_rejected(lib):
     assert app(r(kv), r(bt), FAKE, FAKE, FAKE, FAKE, 8, 0, 1, None) == vx.VX_OK      # nothing new
     assert app(r(kv), r(batch_struct(batch=0)), None, None, None, None, 0, 5, 1,
                None) == vx.VX_OK
+
+
+def test_decode_layers_arguments_rejected(lib):
+    """Every layer is checked before anything is launched: a bad argument in
+    any layer returns its status (with FAKE device pointers a launch would
+    fault, so a pass here also shows that none happened)."""
+    r = ctypes.byref
+    fn = lib.vx_decode_layers
+    n = 3
+    kvs = (vx.PagedKVStruct * n)(*[kv_struct() for _ in range(n)])
+    bt = batch_struct()
+    VPA = ctypes.c_void_p * n
+    qs, outs, sels = VPA(FAKE, FAKE, FAKE), VPA(FAKE, FAKE, FAKE), VPA(FAKE, FAKE, FAKE)
+    dense = (ctypes.c_uint8 * n)(1, 0, 0)
+    st, need = ws_size(lib, vx.VX_OP_DECODE_LAYERS, kvs[0], bt, 32)
+    assert st == 0
+    st_step = ws_size(lib, vx.VX_OP_DECODE_STEP, kvs[0], bt, 32)[1]
+    st_full = ws_size(lib, vx.VX_OP_FULL_DECODE, kvs[0], bt, 32)[1]
+    assert need == max(st_step, st_full)
+
+    def call(kv_arr=kvs, batch=bt, q=qs, layers=n, dn=dense, topk=30, sl=sels, out=outs,
+             ws_bytes=need, scale=0.1):
+        return fn(kv_arr, r(batch), q, layers, dn, topk, 1, 1, 1, scale, sl, out, None, FAKE,
+                  ws_bytes, None)
+
+    assert call(layers=-1) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(layers=0, q=None, out=None, sl=None) == vx.VX_OK
+    assert call(q=None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(sl=None) == vx.VX_ERR_INVALID_ARGUMENT              # layers 1, 2 are sparse
+    assert call(ws_bytes=need - 1) == vx.VX_ERR_WORKSPACE_TOO_SMALL
+    assert call(topk=-1) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(scale=0.0) == vx.VX_ERR_INVALID_ARGUMENT
+    odd = (vx.PagedKVStruct * n)(kv_struct(), kv_struct(), kv_struct(head_dim_qk=64, head_dim_v=64))
+    assert call(kv_arr=odd) == vx.VX_ERR_INVALID_ARGUMENT          # shapes differ between layers
+    bad_last = (vx.PagedKVStruct * n)(kv_struct(), kv_struct(), kv_struct(centroids=None))
+    assert call(kv_arr=bad_last) == vx.VX_ERR_INVALID_ARGUMENT      # the last layer's table
+    late_null = VPA(FAKE, FAKE, None)
+    assert call(out=late_null) == vx.VX_ERR_INVALID_ARGUMENT
+    big = batch_struct(batch=64, max_pages_per_req=2048, max_seq_len=32768)
+    full_big = ws_size(lib, vx.VX_OP_FULL_DECODE, kvs[0], big, 32)[1]
+    assert full_big > 0
+    all_dense = (ctypes.c_uint8 * n)(1, 1, 1)
+    assert call(batch=big, dn=all_dense, sl=None,
+                ws_bytes=full_big - 1) == vx.VX_ERR_WORKSPACE_TOO_SMALL
+    assert call(batch=batch_struct(batch=0)) == vx.VX_OK
