@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-append", action="store_true",
                     help="skip timing the write path (vx_append_kv)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the multi-layer call, eager and as a replayed graph")
     ap.add_argument("--no-radix", action="store_true",
                     help="skip the lossy radix top-k (vx_score_topk_radix) comparison")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -457,6 +459,54 @@ def main():
                 "gbps": (b_rows + b_cent) / (ms * 1e-3) / 1e9}
         log(f"append: {append}")
 
+    # ---------------- every layer in one call (vx_decode_layers), eager and as a
+    # captured graph replayed; all layers sparse, then layer 0 dense (a skipped
+    # layer); step 0's batch throughout
+    graph = None
+    if not args.no_graph:
+        s0 = 0
+        sels_l = [torch.empty_like(sel) for _ in range(nL)]
+        outs_l = [torch.empty_like(out) for _ in range(nL)]
+        lses_l = [torch.empty_like(lse) for _ in range(nL)]
+        ws_l = vx.alloc_workspace(vx.VX_OP_DECODE_LAYERS, kv0, batches[s0], w.k_tot)
+        kvs_l = [lay_i["kv"] for lay_i in layers]
+        qs_l = [lay_i["qs"][s0] for lay_i in layers]
+
+        def make(dense_mask, st):
+            return vx.prepare_decode_layers(kvs_l, batches[s0], qs_l, dense_mask, w.topk, w.n_bos,
+                                            w.n_eos, True, w.sm_scale, sels_l, outs_l, lses_l,
+                                            ws_l, st)
+
+        def time_reps(fn, reps):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t_ = time.perf_counter()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps, (time.perf_counter() - t_) * 1e3 / reps
+
+        graph = {"layers": nL}
+        reps = max(8, min(200, K_steps // nL))
+        for tag, mask in (("all_sparse", [False] * nL), ("layer0_dense", [True] + [False] * (nL - 1))):
+            if tag == "layer0_dense" and args.no_dense:
+                continue
+            r_ = reps if tag == "all_sparse" else max(4, reps // 8)
+            eager = make(mask, stream)
+            e_ms, e_wall = time_reps(eager, r_)
+            g = vx.capture_graph(lambda st, mask=mask: make(mask, st))
+            g_ms, g_wall = time_reps(g.replay, r_)
+            graph[tag] = {"eager_ms_per_pass": e_wall, "graph_ms_per_pass": g_wall,
+                          "eager_stream_ms": e_ms, "graph_stream_ms": g_ms,
+                          "eager_us_per_layer": e_wall * 1e3 / nL,
+                          "graph_us_per_layer": g_wall * 1e3 / nL}
+            del g
+        log(f"layers: {graph}")
+
     # ---------------- dense comparator
     dense = None
     if not args.no_dense:
@@ -521,6 +571,7 @@ def main():
         "separate_calls": separate,
         "radix_topk": radix,
         "append_kv": append,
+        "decode_layers": graph,
         "dense": dense,
     }
     print(json.dumps(line), flush=True)
