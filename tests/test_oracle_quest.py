@@ -1,0 +1,96 @@
+"""Pins of the page-bound (Quest) oracle, oracle/quest.py, against things
+other than itself: the bound's defining property checked by brute force
+against every key, the cases where it is reached exactly, numpy's own
+minimum / maximum for the summary, and a hand-worked example
+(tests/golden/quest_example.json)."""
+
+import json
+import os
+
+import numpy as np
+
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _pages(rng, n=6, H=2, S=16, D=8, scale=1.0):
+    return rng.standard_normal((n, H, S, D)) * scale + rng.standard_normal((n, H, 1, D))
+
+
+def test_summary_is_the_channel_min_and_max():
+    rng = np.random.default_rng(1)
+    k = _pages(rng)
+    b = orc.page_bounds(k)
+    assert np.array_equal(b[:, :, 0], k.min(axis=2))
+    assert np.array_equal(b[:, :, 1], k.max(axis=2))
+
+
+def test_bound_dominates_every_key_of_the_page():
+    rng = np.random.default_rng(2)
+    for trial in range(50):
+        k = _pages(rng, n=5, H=3, S=int(rng.integers(1, 20)), D=int(rng.integers(1, 12)),
+                   scale=10.0 ** rng.uniform(-2, 2))
+        qbar = rng.standard_normal((3, k.shape[3])) * 10.0 ** rng.uniform(-2, 2)
+        s = orc.bound_scores(qbar, orc.page_bounds(k), np.arange(5))        # [H, n]
+        for p in range(5):
+            for h in range(3):
+                best = max(float(qbar[h] @ k[p, h, t]) for t in range(k.shape[2]))
+                assert s[h, p] >= best - 1e-12 * (1 + abs(best))
+
+
+def test_bound_is_reached_for_equal_keys_and_signed_queries():
+    rng = np.random.default_rng(3)
+    D = 16
+    row = rng.standard_normal(D)
+    k = np.broadcast_to(row, (1, 1, 16, D)).copy()               # every key equal
+    q = rng.standard_normal((1, D))
+    assert np.isclose(orc.bound_scores(q, orc.page_bounds(k), [0])[0, 0], q[0] @ row)
+    k = _pages(rng, n=1, H=1, S=16, D=D)
+    b = orc.page_bounds(k)
+    qp = np.abs(rng.standard_normal((1, D)))                     # non-negative query
+    assert np.isclose(orc.bound_scores(qp, b, [0])[0, 0], qp[0] @ k[0, 0].max(axis=0))
+    assert np.isclose(orc.bound_scores(-qp, b, [0])[0, 0], -qp[0] @ k[0, 0].min(axis=0))
+
+
+def test_partial_page_has_no_summary():
+    rng = np.random.default_rng(4)
+    k = _pages(rng, n=3, H=1, S=16, D=4)
+    b = orc.request_bounds(k, 16 * 2 + 5)
+    assert np.all(np.isfinite(b[:2])) and np.all(np.isnan(b[2]))
+
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "quest_example.json")))
+    k = np.array(g["pages"])[:, None]                            # [5, 1, 3, 2]
+    q = np.array(g["q"])
+    assert np.array_equal(orc.group_mean_query(q, 1)[0], g["qbar"])
+    b = orc.page_bounds(k)
+    assert np.array_equal(b[1:4, 0], np.array(g["bounds_of_candidates"]))
+    s = orc.bound_scores(np.array([g["qbar"]]), b, [1, 2, 3])[0]
+    assert s.tolist() == g["criticality_of_candidates"]
+    sel = orc.select_pages_quest(q, b, 5, g["topk"], 1, 1)
+    assert sel[0].tolist() == g["selected"]
+
+
+def test_selection_reserves_unites_and_orders():
+    rng = np.random.default_rng(5)
+    H_kv, G, D, n_b = 2, 4, 8, 30
+    k = _pages(rng, n=n_b, H=H_kv, S=16, D=D)
+    b = orc.page_bounds(k)
+    q = rng.standard_normal((H_kv * G, D))
+    for topk, bos, eos in ((5, 1, 1), (0, 1, 2), (40, 2, 1)):
+        sel = orc.select_pages_quest(q, b, n_b, topk, bos, eos)
+        for h in range(H_kv):
+            assert set(range(bos)) | set(range(n_b - eos, n_b)) <= set(sel[h].tolist())
+            assert len(sel[h]) == min(n_b, topk + bos + eos)
+            assert np.all(np.diff(sel[h]) > 0)
+    # top-k by criticality: every chosen candidate scores at least every other
+    qbar = orc.group_mean_query(q, H_kv)
+    sel = orc.select_pages_quest(q, b, n_b, 7, 1, 1)
+    cand = np.arange(1, n_b - 1)
+    s = orc.bound_scores(qbar, b, cand)
+    for h in range(H_kv):
+        chosen = [p for p in sel[h] if 1 <= p < n_b - 1]
+        rest = [p for p in cand if p not in chosen]
+        assert min(s[h, p - 1] for p in chosen) >= max(s[h, p - 1] for p in rest)
