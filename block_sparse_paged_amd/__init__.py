@@ -33,6 +33,7 @@ VX_OP_DECODE_LAYERS = 4
 
 # Symbols include/vx.h declares (checked by the ABI tests).
 EXPORTS = ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
+           "vx_bounds_update", "vx_score_topk_bounds",
            "vx_sparse_paged_decode",
            "vx_full_paged_decode", "vx_sparse_decode_step", "vx_decode_layers",
            "vx_workspace_size", "vx_set_pages_per_split", "vx_status_string", "vx_version")
@@ -83,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_score_topk.argtypes = [kvp, btp, VP, I32, I32, I32, VP, VP, SZ, VP]
     lib.vx_score_topk_radix.argtypes = [kvp, btp, VP, I32, I32, I32, I32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_paged_decode.argtypes = [kvp, btp, VP, VP, I32, F32, VP, VP, VP, SZ, VP]
+    lib.vx_bounds_update.argtypes = [kvp, VP, VP, I32, VP]
+    lib.vx_score_topk_bounds.argtypes = [kvp, btp, VP, VP, I32, I32, I32, VP, VP, SZ, VP]
     lib.vx_full_paged_decode.argtypes = [kvp, btp, VP, F32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_decode_step.argtypes = [kvp, btp, VP, I32, I32, I32, I32, F32, VP, VP, VP,
                                           VP, SZ, VP]
@@ -94,6 +97,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_status_string.restype = ctypes.c_char_p
     lib.vx_version.argtypes = []
     for name in ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
+                 "vx_bounds_update", "vx_score_topk_bounds",
                  "vx_sparse_paged_decode",
                  "vx_full_paged_decode", "vx_sparse_decode_step", "vx_decode_layers",
                  "vx_workspace_size", "vx_set_pages_per_split", "vx_version"):
@@ -248,6 +252,37 @@ def score_topk_radix(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bo
     _check(load_library().vx_score_topk_radix(
         ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, levels, _ptr(rnd),
         _ptr(sel), _ptr(workspace), workspace.numel(), _stream(stream)), "vx_score_topk_radix")
+
+
+def bounds_update(kv: PagedKV, bounds: torch.Tensor, page_ids: torch.Tensor, stream=None):
+    """vx_bounds_update: per-channel key minimum and maximum of the listed
+    (full) physical pages into ``bounds`` [P, H_kv, 2, D] (Quest's summary)."""
+    _need(bounds, "bounds", kv.k_cache.dtype)
+    _need(page_ids, "page_ids", torch.int32)
+    kvs = kv.struct()
+    _check(load_library().vx_bounds_update(ctypes.byref(kvs), _ptr(bounds), _ptr(page_ids),
+                                           page_ids.numel(), _stream(stream)),
+           "vx_bounds_update")
+
+
+def prepare_score_topk_bounds(kv: PagedKV, batch: Batch, bounds, q, topk, n_bos, n_eos, sel,
+                              workspace, stream=None) -> "PreparedCall":
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    _need(bounds, "bounds", kv.k_cache.dtype)
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(bounds), _ptr(q), topk, n_bos, n_eos,
+            _ptr(sel), _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall(lib.vx_score_topk_bounds, args, "vx_score_topk_bounds",
+                        (kvs, bs, kv, batch, bounds, q, sel, workspace))
+
+
+def score_topk_bounds(kv: PagedKV, batch: Batch, bounds: torch.Tensor, q: torch.Tensor,
+                      topk: int, n_bos: int, n_eos: int, sel: torch.Tensor,
+                      workspace: torch.Tensor, stream=None):
+    """vx_score_topk_bounds: pages selected by Quest's criticality bound."""
+    prepare_score_topk_bounds(kv, batch, bounds, q, topk, n_bos, n_eos, sel, workspace, stream)()
 
 
 def sparse_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sel: torch.Tensor,

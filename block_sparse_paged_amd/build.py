@@ -24,7 +24,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["vx_api.cpp", "vx_centroid.hip", "vx_score_topk.hip", "vx_decode.hip",
-           "vx_decode_mla.hip", "vx_step.hip", "vx_append.hip"]
+           "vx_decode_mla.hip", "vx_step.hip", "vx_append.hip", "vx_quest.hip"]
 
 
 def _compile(src, extra):

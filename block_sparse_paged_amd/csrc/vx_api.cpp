@@ -527,6 +527,87 @@ vx_status vx_append_kv(const vx_paged_kv* kv, const vx_batch* batch, const void*
   return hip_status(launch_append(kv->dtype, a, (int)pages, stream));
 }
 
+vx_status vx_bounds_update(const vx_paged_kv* kv, void* bounds, const int32_t* page_ids,
+                           int32_t n_ids, hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if (n_ids < 0) return VX_ERR_INVALID_ARGUMENT;
+  if (is_mla(kv)) return VX_ERR_UNSUPPORTED;
+  if (n_ids == 0) return VX_OK;
+  if (!bounds || !page_ids || !kv->k_cache) return VX_ERR_INVALID_ARGUMENT;
+  BoundsArgs a{};
+  a.k = kv->k_cache;
+  a.bounds = bounds;
+  a.ids = page_ids;
+  a.n_ids = n_ids;
+  a.H_kv = kv->num_kv_heads;
+  a.S_p = kv->page_size;
+  a.D = kv->head_dim_qk;
+  return hip_status(launch_page_bounds(kv->dtype, a, stream));
+}
+
+vx_status vx_score_topk_bounds(const vx_paged_kv* kv, const vx_batch* batch, const void* bounds,
+                               const void* q, int32_t topk, int32_t n_bos, int32_t n_eos,
+                               int32_t* sel, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (topk < 0 || n_bos < 0 || n_eos < 1) return VX_ERR_INVALID_ARGUMENT;
+  if ((long long)topk + n_bos + n_eos > 0x7fffffffLL) return VX_ERR_INVALID_ARGUMENT;
+  if (is_mla(kv)) return VX_ERR_UNSUPPORTED;
+  const int mp = max_pages_eff(kv, batch);
+  if (mp > kMaxCandidates) return VX_ERR_UNSUPPORTED;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !sel || !bounds || !batch->page_table || !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < score_ws_bytes(kv, batch)) return VX_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return VX_ERR_INVALID_ARGUMENT;
+  const int k_tot = topk + n_bos + n_eos;
+  const int max_cand = std::max(mp - n_bos - n_eos, 0);
+  const bool need_scores = max_cand > topk && topk > 0;   // else all or none are taken
+  float* scores = reinterpret_cast<float*>(workspace);
+  if (need_scores) {
+    ScoreArgs s{};
+    s.q = q;
+    s.cent = bounds;
+    s.pt = batch->page_table;
+    s.seq_lens = batch->seq_lens;
+    s.scores = scores;
+    s.B = batch->batch;
+    s.H_q = batch->num_q_heads;
+    s.H_kv = kv->num_kv_heads;
+    s.D = kv->head_dim_qk;
+    s.S_p = kv->page_size;
+    s.pt_stride = batch->max_pages_per_req;
+    s.score_stride = mp;
+    s.max_tokens = batch->max_seq_len;
+    s.n_bos = n_bos;
+    s.n_eos = n_eos;
+    // the split scorer's cut: about one 8-wave block per CU in all
+    const int nblk = std::max(1, ceil_div(kNumCUs, batch->batch));
+    int cpb = ceil_div(max_cand, nblk);
+    cpb = std::max(32, (cpb + 7) / 8 * 8);
+    s.cand_per_block = cpb;
+    if (launch_bound_score(kv->dtype, s, ceil_div(max_cand, cpb), stream) != hipSuccess)
+      return VX_ERR_HIP;
+  }
+  TopkArgs t{};
+  t.scores = scores;
+  t.seq_lens = batch->seq_lens;
+  t.sel = sel;
+  t.B = batch->batch;
+  t.H_kv = kv->num_kv_heads;
+  t.S_p = kv->page_size;
+  t.score_stride = mp;
+  t.max_tokens = batch->max_seq_len;
+  t.topk = topk;
+  t.n_bos = n_bos;
+  t.n_eos = n_eos;
+  t.k_tot = k_tot;
+  return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
+}
+
 vx_status vx_score_topk(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                         int32_t topk, int32_t n_bos, int32_t n_eos, int32_t* sel,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -126,6 +126,17 @@ hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s
 // the completed pages' centroids (each block's share of the page's rows fits).
 bool score_centroid_fits(int dtype, int D, int H_kv, int grid_x);
 hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s);
+// Page-bound (Quest) rule: the summary rows [P, H_kv, 2, D] (minimum row,
+// then maximum row) of listed pages, and the split scorer of criticality,
+// whose ScoreArgs::cent points at that summary table.
+struct BoundsArgs {
+  const void* k;          // [P, H_kv, S_p, D]
+  void* bounds;           // [P, H_kv, 2, D]
+  const int32_t* ids;     // [n_ids] physical pages
+  int32_t n_ids, H_kv, S_p, D;
+};
+hipError_t launch_page_bounds(int dtype, const BoundsArgs& a, hipStream_t s);
+hipError_t launch_bound_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s);
 // One block per (request, KV head) scores and selects (rows of <= 64 lanes).
 bool fused_indexer_supported(int dtype, int D);
 hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s);

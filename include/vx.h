@@ -205,6 +205,34 @@ vx_status vx_score_topk_radix(const vx_paged_kv* kv, const vx_batch* batch, cons
                               const uint32_t* rnd, int32_t* sel, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* A second page-summary rule through the same pipeline: Quest's key bounds.
+ * The Vortex article (section "Speedups that scale to 229B parameters")
+ * names Quest as the other algorithm it serves without stating its rule;
+ * the rule as the Quest paper gives it (Tang et al., ICML 2024, section 3):
+ * a page is summarised by the per-channel minimum and maximum of its keys,
+ * and its criticality for a query q is sum_i max(q_i * min_i, q_i * max_i),
+ * an upper bound on q . k over the page.
+ *
+ * vx_bounds_update: for each listed physical page p and KV head h,
+ *   bounds[p, h, 0, :] = min over t of K[p, h, t, :]
+ *   bounds[p, h, 1, :] = max over t of K[p, h, t, :]     (exact, KV dtype)
+ *   bounds     device [P, H_kv, 2, D_qk], dtype; only the listed rows written
+ *   page_ids   device int32 [n_ids], each in [0, num_pages), full pages;
+ *              n_ids >= 0 (0 launches nothing)
+ *
+ * vx_score_topk_bounds: vx_score_topk with the criticality above in place of
+ * the centroid score (q is the group mean of the KV head's query heads, as
+ * there); reserved pages, ties, order, padding, workspace
+ * (VX_OP_SCORE_TOPK's size) and errors as vx_score_topk.  The selection
+ * feeds vx_sparse_paged_decode unchanged.
+ * Both: D_qk in {64, 128} (MLA shapes return VX_ERR_UNSUPPORTED). */
+vx_status vx_bounds_update(const vx_paged_kv* kv, void* bounds, const int32_t* page_ids,
+                           int32_t n_ids, hipStream_t stream);
+vx_status vx_score_topk_bounds(const vx_paged_kv* kv, const vx_batch* batch, const void* bounds,
+                               const void* q, int32_t topk, int32_t n_bos, int32_t n_eos,
+                               int32_t* sel, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Sparse attention over the selected pages (article, "A dual-stage
  * programmable abstraction": after selecting the top-k blocks the system
  * performs the actual attention on them).

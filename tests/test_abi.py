@@ -313,3 +313,28 @@ def test_decode_layers_arguments_rejected(lib):
     assert call(batch=big, dn=all_dense, sl=None,
                 ws_bytes=full_big - 1) == vx.VX_ERR_WORKSPACE_TOO_SMALL
     assert call(batch=batch_struct(batch=0)) == vx.VX_OK
+
+
+def test_bounds_arguments_rejected(lib):
+    r = ctypes.byref
+    kv, bt = kv_struct(), batch_struct()
+    upd, score = lib.vx_bounds_update, lib.vx_score_topk_bounds
+    assert upd(r(kv), FAKE, FAKE, -1, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert upd(r(kv), None, FAKE, 4, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert upd(r(kv), FAKE, None, 4, None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert upd(r(kv), None, None, 0, None) == vx.VX_OK                   # nothing to do
+    mla = kv_struct(head_dim_qk=576, head_dim_v=512, num_kv_heads=1, page_size=64,
+                    v_aliases_k=1, v_cache=None)
+    assert upd(r(mla), FAKE, FAKE, 4, None) == vx.VX_ERR_UNSUPPORTED
+    need = ws_size(lib, vx.VX_OP_SCORE_TOPK, kv, bt)[1]
+    for args, want in (((FAKE, FAKE, 30, 1, 0, FAKE, FAKE, need), vx.VX_ERR_INVALID_ARGUMENT),
+                       ((FAKE, FAKE, -1, 1, 1, FAKE, FAKE, need), vx.VX_ERR_INVALID_ARGUMENT),
+                       ((None, FAKE, 30, 1, 1, FAKE, FAKE, need), vx.VX_ERR_INVALID_ARGUMENT),
+                       ((FAKE, None, 30, 1, 1, FAKE, FAKE, need), vx.VX_ERR_INVALID_ARGUMENT),
+                       ((FAKE, FAKE, 30, 1, 1, FAKE, FAKE, need - 1), vx.VX_ERR_WORKSPACE_TOO_SMALL)):
+        assert score(r(kv), r(bt), *args, None) == want
+    mbt = batch_struct(num_q_heads=32, max_seq_len=64 * 64)
+    assert score(r(mla), r(mbt), FAKE, FAKE, 30, 1, 1, FAKE, FAKE, 1 << 30,
+                 None) == vx.VX_ERR_UNSUPPORTED
+    assert score(r(kv), r(batch_struct(batch=0)), None, None, 30, 1, 1, None, None, 0,
+                 None) == vx.VX_OK

@@ -1,0 +1,125 @@
+"""GPU parity of the second page-summary rule (Quest's key bounds) through
+the same pipeline: vx_bounds_update against the oracle's per-channel
+minimum and maximum (exact), vx_score_topk_bounds against the oracle's
+selection by criticality (bit-exact where the k-th and (k+1)-th
+criticalities are apart by more than fp32 scoring can blur, else the
+selection must be a valid top-k of the oracle's scores), and the attention
+over that selection."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle as orc
+from tests import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_paged_amd as m
+    m.load_library()
+    m.set_pages_per_split(0)
+    return m
+
+
+def _case(vx, w):
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    bounds = torch.zeros((c.layout.num_pages, w.num_kv_heads, 2, w.head_dim_qk),
+                         dtype=w.torch_dtype, device="cuda")
+    ids = np.concatenate([synth.setup_full_pages(c.layout), synth.completed_pages(c.layout, 0)])
+    vx.bounds_update(c.kv, bounds, torch.from_numpy(ids.astype(np.int32)).cuda())
+    return c, bounds, ids
+
+
+def _check_selection(c, b, bounds_dev, sel_dev, exact_counter):
+    """Selection of request b against the oracle's criticalities."""
+    w = c.w
+    k_pages, _ = c.request_pages(b)
+    L = int(c.L[b])
+    n_b = -(-L // w.page_size)
+    bnd = orc.request_bounds(k_pages, L)[:n_b]
+    want = orc.select_pages_quest(c.q_host[b].double().numpy(), bnd, n_b, w.topk, w.n_bos, w.n_eos)
+    got = sel_dev[b].cpu().numpy()
+    cand = orc.candidate_pages(n_b, w.n_bos, w.n_eos)
+    qbar = orc.group_mean_query(c.q_host[b].double().numpy(), w.num_kv_heads)
+    s = orc.bound_scores(qbar, bnd, cand) if len(cand) else None
+    for h in range(w.num_kv_heads):
+        g = got[h][got[h] >= 0]
+        if np.array_equal(g, want[h]):
+            exact_counter[0] += 1
+            continue
+        # different sets are acceptable only when fp32 scoring cannot tell
+        # the boundary candidates apart
+        assert s is not None and len(cand) > w.topk, f"request {b} head {h}: selection differs"
+        order = np.sort(s[h])[::-1]
+        gap = order[w.topk - 1] - order[w.topk]
+        tol = 1e-5 * np.abs(s[h]).max()
+        assert gap <= tol, f"request {b} head {h}: selection differs with a clear gap {gap:.3g}"
+        chosen = np.isin(cand, g)
+        assert chosen.sum() == w.topk
+        assert s[h][chosen].min() >= s[h][~chosen].max() - tol
+        exact_counter[1] += 1
+
+
+@pytest.mark.parametrize("name", ["qwen3_small", "long_small", "hetero_small", "tiny_b1_l1k_f32"])
+def test_bounds_small(vx, name):
+    w = synth.get_workload(name)
+    c, bounds, ids = _case(vx, w)
+    torch.cuda.synchronize()
+    got = H.to_f64(bounds[torch.from_numpy(ids.astype(np.int64)).cuda()])
+    want = orc.page_bounds(H.to_f64(c.K[torch.from_numpy(ids.astype(np.int64)).cuda()]))
+    assert np.array_equal(got, want), "page bounds differ"
+    bt = c.batch(vx)
+    sel = torch.full((w.batch, w.num_kv_heads, w.k_tot), -7, dtype=torch.int32, device="cuda")
+    ws = vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, c.kv, bt)
+    q = c.q_host.cuda()
+    vx.score_topk_bounds(c.kv, bt, bounds, q, w.topk, w.n_bos, w.n_eos, sel, ws)
+    out, lse = H.run_sparse(vx, c, q, sel)
+    torch.cuda.synchronize()
+    counts = [0, 0]
+    for b in range(w.batch):
+        _check_selection(c, b, bounds, sel, counts)
+        k, v = c.request_pages(b)
+        s_rows = sel[b].cpu().numpy()
+        picked = [r[r >= 0] for r in s_rows]
+        o_ref, lse_ref = orc.decode_request(c.q_host[b].double().numpy(), k, v, int(c.L[b]),
+                                            w.sm_scale, picked,
+                                            v_dims=w.head_dim_v if v is None else None)
+        H.assert_close_out(H.to_f64(out[b]), o_ref, w.dtype, f"request {b} out")
+        H.assert_close_lse(H.to_f64(lse[b]), lse_ref, w.dtype, f"request {b}")
+    H.log(f"  units exact {counts[0]}, within fp32 blur {counts[1]}")
+    assert counts[0] >= 0.9 * sum(counts)
+
+
+def test_bounds_full_size_sampled(vx):
+    """The Qwen-like layer at full size (32 requests of 32768 tokens): the
+    summary of every full page, the selection of two sampled requests."""
+    w = synth.get_workload("qwen3_0p6b_b32_l32k")
+    c, bounds, ids = _case(vx, w)
+    bt = c.batch(vx)
+    sel = torch.full((w.batch, w.num_kv_heads, w.k_tot), -7, dtype=torch.int32, device="cuda")
+    ws = vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, c.kv, bt)
+    vx.score_topk_bounds(c.kv, bt, bounds, c.q_host.cuda(), w.topk, w.n_bos, w.n_eos, sel, ws)
+    torch.cuda.synchronize()
+    counts = [0, 0]
+    for b in (0, w.batch - 1):
+        n_b = -(-int(c.L[b]) // w.page_size)
+        phys = torch.from_numpy(c.layout.page_table[b, :int(c.L[b]) // w.page_size].astype(np.int64)).cuda()
+        assert np.array_equal(H.to_f64(bounds[phys]), orc.page_bounds(H.to_f64(c.K[phys])))
+        _check_selection(c, b, bounds, sel, counts)
+        assert n_b > w.k_tot
+    assert counts[0] >= 0.9 * sum(counts)
+
+
+def test_bounds_rejects_mla(vx):
+    w = synth.get_workload("mla_small")
+    c = H.setup_case(vx, w)
+    bounds = torch.zeros((c.layout.num_pages, 1, 2, 576), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(vx.VxError) as e:
+        vx.bounds_update(c.kv, bounds, torch.zeros(1, dtype=torch.int32, device="cuda"))
+    assert e.value.status == vx.VX_ERR_UNSUPPORTED
