@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-append", action="store_true",
                     help="skip timing the write path (vx_append_kv)")
+    ap.add_argument("--no-bounds", action="store_true",
+                    help="skip the second summary rule (per-page key bounds)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the multi-layer call, eager and as a replayed graph")
     ap.add_argument("--no-radix", action="store_true",
@@ -459,6 +461,70 @@ def main():
                 "gbps": (b_rows + b_cent) / (ms * 1e-3) / 1e9}
         log(f"append: {append}")
 
+    # ---------------- the second summary rule: per-page key bounds (Quest's
+    # criticality) against the centroid indexer, same steps and layers
+    bounds_sec = None
+    if not args.no_bounds and not w.v_aliases_k:
+        setup_bnd = [torch.zeros((lay.num_pages, w.num_kv_heads, 2, w.head_dim_qk),
+                                 dtype=w.torch_dtype, device=dev) for _ in layers]
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for tab, lay_i in zip(setup_bnd, layers):        # cache construction (setup)
+            vx.bounds_update(lay_i["kv"], tab, setup_ids, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        build_ms = e0.elapsed_time(e1) / len(setup_bnd)
+        sel_b = torch.empty_like(sel)
+        prep_b = {}
+
+        def pick_b(i):
+            key = (i % nL, i % T)
+            if key not in prep_b:
+                kv, bt, q = layers[key[0]]["kv"], batches[key[1]], layers[key[0]]["qs"][key[1]]
+                prep_b[key] = vx.prepare_score_topk_bounds(kv, bt, setup_bnd[key[0]], q, w.topk,
+                                                           w.n_bos, w.n_eos, sel_b, ws_idx, stream)
+            return prep_b[key]
+
+        def time_pick(pick):
+            for i in range(min(W_steps, 8)):
+                pick(i)()
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for i in range(n_sep):
+                pick(W_steps + i)()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / n_sep
+
+        ms_c = time_pick(lambda i: schedule(i)["idx"])
+        ms_b = time_pick(pick_b)
+        overlap = []
+        for i in range(min(nL * T, 8)):
+            schedule(i)["idx"]()
+            pick_b(i)()
+            torch.cuda.synchronize()
+            s_ = i % T
+            e_tab, b_tab = sel.cpu().numpy(), sel_b.cpu().numpy()
+            for bq in range(w.batch):
+                n_b = -(-int(L_steps[s_][bq]) // w.page_size)
+                res = set(range(min(w.n_bos, n_b))) | set(range(max(n_b - w.n_eos, 0), n_b))
+                for h in range(w.num_kv_heads):
+                    E = set(e_tab[bq, h][e_tab[bq, h] >= 0].tolist()) - res
+                    Bs = set(b_tab[bq, h][b_tab[bq, h] >= 0].tolist()) - res
+                    if E:
+                        overlap.append(len(E & Bs) / len(E))
+        # the indexer's bytes with two summary rows per candidate instead of one
+        rows = np.mean([sum(max(-(-int(Lb) // w.page_size) - w.n_bos - w.n_eos, 0) for Lb in L_steps[s])
+                        for s in sched]) * w.num_kv_heads * w.head_dim_qk * w.elem_bytes
+        b_bnd = b_idx + rows
+        bounds_sec = {"indexer_ms": ms_b, "centroid_indexer_ms": ms_c, "bytes_per_call": int(b_bnd),
+                      "gbps": b_bnd / (ms_b * 1e-3) / 1e9,
+                      "setup_build_ms_per_layer": build_ms,
+                      "overlap_with_centroid_topk": float(np.mean(overlap))}
+        log(f"page bounds: {bounds_sec}")
+
     # ---------------- every layer in one call (vx_decode_layers), eager and as a
     # captured graph replayed; all layers sparse, then layer 0 dense (a skipped
     # layer); step 0's batch throughout
@@ -571,6 +637,7 @@ def main():
         "separate_calls": separate,
         "radix_topk": radix,
         "append_kv": append,
+        "page_bounds": bounds_sec,
         "decode_layers": graph,
         "dense": dense,
     }

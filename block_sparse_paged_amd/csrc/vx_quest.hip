@@ -115,6 +115,12 @@ __global__ __launch_bounds__(kBoundScoreThreads) void bound_score_kernel(ScoreAr
     return ((size_t)phys[c] * a.H_kv + h) * 2 * D + seg * E;
   };
   float* out = a.scores + (size_t)b * a.H_kv * a.score_stride;
+  // with H_kv dividing STEP every row of a lane has the same KV head, whose
+  // query segment then stays in registers
+  const bool fixed_head = STEP % a.H_kv == 0;
+  float qr[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qr[e] = qbar[(rw % a.H_kv) * D + seg * E + e];
   uint4 lo[U], hi[U];
   if (nbat > 0) {
 #pragma unroll
@@ -140,10 +146,15 @@ __global__ __launch_bounds__(kBoundScoreThreads) void bound_score_kernel(ScoreAr
       V::unpack(hi[u], fh);
       lo[u] = ld16(bnd + nx[u]);
       hi[u] = ld16(bnd + nx[u] + D);
-      const float* qh = qbar + h * D + seg * E;
       float acc = 0.f;
+      if (fixed_head) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc += fmaxf(qh[e] * fl[e], qh[e] * fh[e]);
+        for (int e = 0; e < E; ++e) acc += fmaxf(qr[e] * fl[e], qr[e] * fh[e]);
+      } else {
+        const float* qh = qbar + h * D + seg * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += fmaxf(qh[e] * fl[e], qh[e] * fh[e]);
+      }
       acc = lane_group_sum<LH>(acc);
       if (seg == u) mine = acc;
     }
