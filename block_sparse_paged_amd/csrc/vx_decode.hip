@@ -26,6 +26,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeArgs a) {
   constexpr int NT = kNW * 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // with a selection to make, the first share of the scores row goes out
+  // before the request length is known (entries past the request's
+  // candidates are read and ignored)
+  constexpr int kIn = 16;              // score loads in flight per thread
+  float v0[kIn];
+  if constexpr (SELECT) {
+    const float* sc = a.scores + ((size_t)b * a.H_kv + h) * a.score_stride;
+#pragma unroll
+    for (int j = 0; j < kIn; ++j) v0[j] = sc[min(tid + j * NT, a.score_stride - 1)];
+  }
   int seq = a.seq_lens[b];
   seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
   const int n_b = (seq + a.S_p - 1) / a.S_p;
@@ -42,11 +52,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeArgs a) {
     __syncthreads();
     if (n_cand > a.topk && a.topk > 0) {
       const float* sc = a.scores + ((size_t)b * a.H_kv + h) * a.score_stride;
-      constexpr int kIn = 16;          // score loads in flight per thread
       for (int i0 = tid; i0 < n_cand; i0 += kIn * NT) {
         float v[kIn];
 #pragma unroll
-        for (int j = 0; j < kIn; ++j) v[j] = sc[min(i0 + j * NT, n_cand - 1)];
+        for (int j = 0; j < kIn; ++j) v[j] = i0 == tid ? v0[j] : sc[min(i0 + j * NT, n_cand - 1)];
 #pragma unroll
         for (int j = 0; j < kIn; ++j) {
           const int i = i0 + j * NT;
