@@ -123,3 +123,33 @@ def test_bounds_rejects_mla(vx):
     with pytest.raises(vx.VxError) as e:
         vx.bounds_update(c.kv, bounds, torch.zeros(1, dtype=torch.int32, device="cuda"))
     assert e.value.status == vx.VX_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("topk,bos,eos", [(4, 1, 1), (0, 1, 1), (3, 0, 2)])
+@pytest.mark.parametrize("dtype,D,G,S", [("f32", 64, 1, 16), ("bf16", 128, 8, 16),
+                                         ("bf16", 64, 4, 64), ("f32", 128, 2, 16)])
+def test_bounds_edge_lengths(vx, dtype, D, G, S, topk, bos, eos):
+    """Ragged and tiny requests (fewer candidates than k, none at all, a
+    partial last page) through the bound indexer and the attention."""
+    lens = (1, S - 1, S, S + 1, S * 6, S * 6 + 1, S * 9 + 3)
+    w = synth.Workload(name="edges", batch=len(lens), num_q_heads=2 * G, num_kv_heads=2,
+                       head_dim_qk=D, head_dim_v=D, page_size=S, dtype=dtype, topk=topk,
+                       structure="page_offset", seed=81, seq_lens=lens, n_bos=bos, n_eos=eos,
+                       spare_pages=5)
+    c, bounds, ids = _case(vx, w)
+    bt = c.batch(vx)
+    sel = torch.full((w.batch, w.num_kv_heads, w.k_tot), -7, dtype=torch.int32, device="cuda")
+    ws = vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, c.kv, bt)
+    q = c.q_host.cuda()
+    vx.score_topk_bounds(c.kv, bt, bounds, q, w.topk, w.n_bos, w.n_eos, sel, ws)
+    out, lse = H.run_sparse(vx, c, q, sel)
+    torch.cuda.synchronize()
+    counts = [0, 0]
+    for b in range(w.batch):
+        _check_selection(c, b, bounds, sel, counts)
+        k, v = c.request_pages(b)
+        picked = [r[r >= 0] for r in sel[b].cpu().numpy()]
+        o_ref, lse_ref = orc.decode_request(c.q_host[b].double().numpy(), k, v, int(c.L[b]),
+                                            w.sm_scale, picked)
+        H.assert_close_out(H.to_f64(out[b]), o_ref, w.dtype, f"request {b} out")
+        H.assert_close_lse(H.to_f64(lse[b]), lse_ref, w.dtype, f"request {b}")
