@@ -16,6 +16,11 @@
  * Full attention over every page is the baseline the method is measured
  * against, and what a skipped layer runs (README, "Using Your Sparse
  * Attention with SGLang")                                    -> vx_full_paged_decode
+ * Around them: the whole step fused (vx_sparse_decode_step), every layer of
+ * a step in one capturable call (vx_decode_layers), the write path with
+ * centroids on completion (vx_append_kv), the lossy radix indexer
+ * (vx_score_topk_radix) and a second summary rule, Quest's key bounds
+ * (vx_bounds_update, vx_score_topk_bounds).
  *
  * Conventions shared by every call
  *   Pointers.   Every buffer pointer is a DEVICE pointer unless marked
