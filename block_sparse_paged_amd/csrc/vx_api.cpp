@@ -567,6 +567,42 @@ vx_status vx_score_topk_bounds(const vx_paged_kv* kv, const vx_batch* batch, con
   const int max_cand = std::max(mp - n_bos - n_eos, 0);
   const bool need_scores = max_cand > topk && topk > 0;   // else all or none are taken
   float* scores = reinterpret_cast<float*>(workspace);
+  TopkArgs t{};
+  t.scores = scores;
+  t.seq_lens = batch->seq_lens;
+  t.sel = sel;
+  t.B = batch->batch;
+  t.H_kv = kv->num_kv_heads;
+  t.S_p = kv->page_size;
+  t.score_stride = mp;
+  t.max_tokens = batch->max_seq_len;
+  t.topk = topk;
+  t.n_bos = n_bos;
+  t.n_eos = n_eos;
+  t.k_tot = k_tot;
+  // as the centroid indexer: one block per (request, KV head) scoring and
+  // selecting when such blocks fill the GPU, else the split scorer + K3
+  const long long units = (long long)batch->batch * kv->num_kv_heads;
+  if (fused_indexer_supported(kv->dtype, kv->head_dim_qk) && mp <= kFusedMaxPages &&
+      (units >= kNumCUs / 2 || units * mp <= 4096)) {
+    ScoreArgs s{};
+    s.q = q;
+    s.cent = bounds;
+    s.pt = batch->page_table;
+    s.seq_lens = batch->seq_lens;
+    s.B = batch->batch;
+    s.H_q = batch->num_q_heads;
+    s.H_kv = kv->num_kv_heads;
+    s.D = kv->head_dim_qk;
+    s.S_p = kv->page_size;
+    s.pt_stride = batch->max_pages_per_req;
+    s.score_stride = mp;
+    s.max_tokens = batch->max_seq_len;
+    s.n_bos = n_bos;
+    s.n_eos = n_eos;
+    s.scores = scores;     // not read by the fused kernel
+    return hip_status(launch_indexer_fused(kv->dtype, s, t, stream, true));
+  }
   if (need_scores) {
     ScoreArgs s{};
     s.q = q;
@@ -592,19 +628,6 @@ vx_status vx_score_topk_bounds(const vx_paged_kv* kv, const vx_batch* batch, con
     if (launch_bound_score(kv->dtype, s, ceil_div(max_cand, cpb), stream) != hipSuccess)
       return VX_ERR_HIP;
   }
-  TopkArgs t{};
-  t.scores = scores;
-  t.seq_lens = batch->seq_lens;
-  t.sel = sel;
-  t.B = batch->batch;
-  t.H_kv = kv->num_kv_heads;
-  t.S_p = kv->page_size;
-  t.score_stride = mp;
-  t.max_tokens = batch->max_seq_len;
-  t.topk = topk;
-  t.n_bos = n_bos;
-  t.n_eos = n_eos;
-  t.k_tot = k_tot;
   return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
 }
 

@@ -137,9 +137,11 @@ struct BoundsArgs {
 };
 hipError_t launch_page_bounds(int dtype, const BoundsArgs& a, hipStream_t s);
 hipError_t launch_bound_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s);
-// One block per (request, KV head) scores and selects (rows of <= 64 lanes).
+// One block per (request, KV head) scores and selects (rows of <= 64 lanes);
+// with bounds, a.cent is the key-bounds table and the score Quest's bound.
 bool fused_indexer_supported(int dtype, int D);
-hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s);
+hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s,
+                                bool bounds = false);
 // D = D_qk = D_v for this path; G = H_q / H_kv.
 hipError_t launch_decode_split(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);

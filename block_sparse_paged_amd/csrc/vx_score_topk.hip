@@ -41,7 +41,7 @@ constexpr int kSplitLoads = 8;      // wave-loads in flight per lane in the spli
 constexpr int kScoreCentroidPairs = 2 * kScoreThreads;
 
 // ---------------------------------------------------------------- fused
-template <typename T, int D>
+template <typename T, int D, bool BOUNDS>
 __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs a, TopkArgs t) {
   extern __shared__ __align__(16) uint32_t dyn[];   // phys, keys: round4(max_cand) each
   __shared__ float qbar[D];
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_fused_kernel(ScoreArgs 
   select_init<kFusedThreads>(sl);
   __syncthreads();
 
-  if (scoring) score_head<T, D, kFusedThreads>(a, h, n_cand, phys, qbar, keys, sl);
+  if (scoring) score_head<T, D, kFusedThreads, BOUNDS>(a, h, n_cand, phys, qbar, keys, sl);
   select_pages<kFusedThreads>(keys, n_cand, n_b, t.topk, t.n_bos, t.n_eos, t.k_tot,
                               t.sel + ((size_t)b * t.H_kv + h) * t.k_tot, nullptr, sl, t.levels,
                               t.rnd ? t.rnd[(size_t)b * t.H_kv + h] : 0u);
@@ -400,10 +400,14 @@ hipError_t run_score(const ScoreArgs& a, int grid_x, hipStream_t s) {
 }
 
 template <typename T, int D>
-hipError_t run_fused(const ScoreArgs& a, const TopkArgs& t, hipStream_t s) {
+hipError_t run_fused(const ScoreArgs& a, const TopkArgs& t, bool bounds, hipStream_t s) {
   const size_t lds = 2 * (size_t)round4(a.score_stride > 0 ? a.score_stride : 1) * sizeof(uint32_t);
-  hipLaunchKernelGGL((indexer_fused_kernel<T, D>), dim3(a.H_kv, a.B), dim3(kFusedThreads), lds, s,
-                     a, t);
+  if (bounds)
+    hipLaunchKernelGGL((indexer_fused_kernel<T, D, true>), dim3(a.H_kv, a.B), dim3(kFusedThreads),
+                       lds, s, a, t);
+  else
+    hipLaunchKernelGGL((indexer_fused_kernel<T, D, false>), dim3(a.H_kv, a.B), dim3(kFusedThreads),
+                       lds, s, a, t);
   return hipGetLastError();
 }
 
@@ -448,16 +452,17 @@ hipError_t launch_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s) {
+hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t, hipStream_t s,
+                                bool bounds) {
   if (dtype == 0) {
     switch (a.D) {
-      case 64: return run_fused<float, 64>(a, t, s);
-      case 128: return run_fused<float, 128>(a, t, s);
+      case 64: return run_fused<float, 64>(a, t, bounds, s);
+      case 128: return run_fused<float, 128>(a, t, bounds, s);
     }
   } else {
     switch (a.D) {
-      case 64: return run_fused<bf16_t, 64>(a, t, s);
-      case 128: return run_fused<bf16_t, 128>(a, t, s);
+      case 64: return run_fused<bf16_t, 64>(a, t, bounds, s);
+      case 128: return run_fused<bf16_t, 128>(a, t, bounds, s);
     }
   }
   return hipErrorInvalidValue;

@@ -379,7 +379,11 @@ __device__ __forceinline__ void head_query_mean(const ScoreArgs& a, int b, int h
 constexpr int kScoreLoads = 16;
 constexpr int kScoreLoadsShared = 6;
 
-template <typename T, int D, int NT>
+// BOUNDS: the summary is two rows per (page, head) [P, H_kv, 2, D] (the
+// per-channel key minimum, then maximum) and the score is Quest's
+// criticality sum_e max(q_e * min_e, q_e * max_e); both rows of a candidate
+// are loaded together.
+template <typename T, int D, int NT, bool BOUNDS = false>
 __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand,
                                            const int32_t* phys, const float* qbar,
                                            uint32_t* keys, SelectLds<NT>& S) {
@@ -396,8 +400,9 @@ __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand
   float qr[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) qr[e] = qbar[seg * E + e];
-  const T* cent = reinterpret_cast<const T*>(a.cent) + (size_t)h * D + seg * E;
-  const size_t pstride = (size_t)a.H_kv * D;
+  constexpr int RS = BOUNDS ? 2 : 1;         // summary rows per (page, head)
+  const T* cent = reinterpret_cast<const T*>(a.cent) + (size_t)h * RS * D + seg * E;
+  const size_t pstride = (size_t)a.H_kv * RS * D;
   const int last = n_cand - 1;
   for (int bi = w;;) {                       // batch bi: candidates [bi * ROWS, +ROWS)
     const int r0 = bi * ROWS;
@@ -408,17 +413,27 @@ __device__ __forceinline__ void score_head(const ScoreArgs& a, int h, int n_cand
     int ph[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) ph[u] = phys[min(c0 + u, last)];
-    uint4 buf[U];
+    uint4 buf[U], hib[BOUNDS ? U : 1];
 #pragma unroll
-    for (int u = 0; u < U; ++u) buf[u] = ld16(cent + (size_t)ph[u] * pstride);
+    for (int u = 0; u < U; ++u) {
+      buf[u] = ld16(cent + (size_t)ph[u] * pstride);
+      if constexpr (BOUNDS) hib[u] = ld16(cent + (size_t)ph[u] * pstride + D);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u;
       float f[E];
       V::unpack(buf[u], f);
       float acc = 0.f;
+      if constexpr (BOUNDS) {
+        float fh[E];
+        V::unpack(hib[u], fh);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc = fmaf(qr[e], f[e], acc);
+        for (int e = 0; e < E; ++e) acc += fmaxf(qr[e] * f[e], qr[e] * fh[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc = fmaf(qr[e], f[e], acc);
+      }
       acc = lane_group_sum<LH>(acc);
       if (c < n_cand && seg == 0) {
         const uint32_t k = order_key(acc);
