@@ -705,3 +705,26 @@ def test_selection_beyond_register_keys_4_wave_blocks(vx):
     assert torch.equal(sel, H.run_indexer(vx, c, q))
     for b in reqs:
         _check_request(vx, c, b, sel, out, lse)
+
+
+def test_maximum_candidates(vx):
+    """The largest request the library takes: 16384 pages (262,144 tokens of
+    16-token pages), next to a short one, through the indexer and the decode
+    step (split scorer, selection inside the split decode reading its keys
+    from LDS); both match the oracle."""
+    lens = (16 * 16384, 16 * 37 + 9)
+    w = synth.Workload(name="max_cand", batch=len(lens), num_q_heads=2, num_kv_heads=1,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, dtype="bf16", topk=64,
+                       structure="page_offset", seed=89, seq_lens=lens, spare_pages=2)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    assert -(-int(c.batch(vx).max_seq_len) // 16) == 16384
+    H.build_setup_centroids(vx, c)
+    H.fix_gaps(c, range(w.batch))
+    q = c.q_host.cuda()
+    sel = H.run_indexer(vx, c, q)
+    sel2, out2, lse2 = H.run_step(vx, c, q, update=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2)
+    for b in range(w.batch):
+        _check_request(vx, c, b, sel2, out2, lse2)
