@@ -343,6 +343,15 @@ hipError_t launch_completed_centroids(const vx_paged_kv* kv, const vx_batch* bat
 // `scores`.  With update_completed it also writes the completed pages'
 // centroids (in the kernel when each block's share of a page fits, else with
 // the centroid kernel first).
+// Candidates per block of a split scorer (K2, K9): about one 8-wave block
+// per CU in all, each request's candidates cut into ceil(256 / B) chunks (a
+// multiple of 8 pages, at least 32).
+int split_score_chunk(const vx_batch* batch, int max_cand) {
+  const int nblk = std::max(1, ceil_div(kNumCUs, batch->batch));
+  const int cpb = ceil_div(max_cand, nblk);
+  return std::max(32, (cpb + 7) / 8 * 8);
+}
+
 hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
                               int32_t n_bos, int32_t n_eos, float* scores, bool update_completed,
                               hipStream_t stream) {
@@ -365,11 +374,7 @@ hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, cons
     s.max_tokens = batch->max_seq_len;
     s.n_bos = n_bos;
     s.n_eos = n_eos;
-    // about one 8-wave block per CU in all: each request's candidates are
-    // cut into ceil(256 / B) chunks (a multiple of 8 pages, at least 32)
-    const int nblk = std::max(1, ceil_div(kNumCUs, batch->batch));
-    int cpb = ceil_div(max_cand, nblk);
-    cpb = std::max(32, (cpb + 7) / 8 * 8);
+    const int cpb = split_score_chunk(batch, max_cand);
     s.cand_per_block = cpb;
     const int grid_x = ceil_div(max_cand, cpb);
     if (update_completed) {
@@ -620,10 +625,7 @@ vx_status vx_score_topk_bounds(const vx_paged_kv* kv, const vx_batch* batch, con
     s.max_tokens = batch->max_seq_len;
     s.n_bos = n_bos;
     s.n_eos = n_eos;
-    // the split scorer's cut: about one 8-wave block per CU in all
-    const int nblk = std::max(1, ceil_div(kNumCUs, batch->batch));
-    int cpb = ceil_div(max_cand, nblk);
-    cpb = std::max(32, (cpb + 7) / 8 * 8);
+    const int cpb = split_score_chunk(batch, max_cand);
     s.cand_per_block = cpb;
     if (launch_bound_score(kv->dtype, s, ceil_div(max_cand, cpb), stream) != hipSuccess)
       return VX_ERR_HIP;
