@@ -500,6 +500,21 @@ def main():
 
         ms_c = time_pick(lambda i: schedule(i)["idx"])
         ms_b = time_pick(pick_b)
+        # the whole step under the bound rule (vx_sparse_decode_step_bounds,
+        # with the completed pages' bounds), beside the centroid rule's step
+        prep_s = {}
+
+        def pick_s(i):
+            key = (i % nL, i % T)
+            if key not in prep_s:
+                kv, bt, q = layers[key[0]]["kv"], batches[key[1]], layers[key[0]]["qs"][key[1]]
+                prep_s[key] = vx.prepare_sparse_decode_step_bounds(
+                    kv, bt, setup_bnd[key[0]], q, w.topk, w.n_bos, w.n_eos, True, w.sm_scale,
+                    sel_b, out, lse, ws_step, stream)
+            return prep_s[key]
+
+        ms_sc = time_pick(lambda i: schedule(i)["step"])
+        ms_sb = time_pick(pick_s)
         overlap = []
         for i in range(min(nL * T, 8)):
             schedule(i)["idx"]()
@@ -519,8 +534,11 @@ def main():
         rows = np.mean([sum(max(-(-int(Lb) // w.page_size) - w.n_bos - w.n_eos, 0) for Lb in L_steps[s])
                         for s in sched]) * w.num_kv_heads * w.head_dim_qk * w.elem_bytes
         b_bnd = b_idx + rows
+        b_sb = b_step + rows
         bounds_sec = {"indexer_ms": ms_b, "centroid_indexer_ms": ms_c, "bytes_per_call": int(b_bnd),
                       "gbps": b_bnd / (ms_b * 1e-3) / 1e9,
+                      "step_ms": ms_sb, "centroid_step_ms": ms_sc, "step_bytes": int(b_sb),
+                      "step_gbps": b_sb / (ms_sb * 1e-3) / 1e9,
                       "setup_build_ms_per_layer": build_ms,
                       "overlap_with_centroid_topk": float(np.mean(overlap))}
         log(f"page bounds: {bounds_sec}")

@@ -35,7 +35,8 @@ VX_OP_DECODE_LAYERS = 4
 EXPORTS = ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
            "vx_bounds_update", "vx_score_topk_bounds",
            "vx_sparse_paged_decode",
-           "vx_full_paged_decode", "vx_sparse_decode_step", "vx_decode_layers",
+           "vx_full_paged_decode", "vx_sparse_decode_step", "vx_sparse_decode_step_bounds",
+           "vx_decode_layers",
            "vx_workspace_size", "vx_set_pages_per_split", "vx_status_string", "vx_version")
 
 
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_full_paged_decode.argtypes = [kvp, btp, VP, F32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_decode_step.argtypes = [kvp, btp, VP, I32, I32, I32, I32, F32, VP, VP, VP,
                                           VP, SZ, VP]
+    lib.vx_sparse_decode_step_bounds.argtypes = [kvp, btp, VP, VP, I32, I32, I32, I32, F32, VP,
+                                                 VP, VP, VP, SZ, VP]
     lib.vx_decode_layers.argtypes = [kvp, btp, VP, I32, VP, I32, I32, I32, I32, F32, VP, VP, VP,
                                      VP, SZ, VP]
     lib.vx_workspace_size.argtypes = [I32, kvp, btp, I32, P(SZ)]
@@ -99,7 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk_radix",
                  "vx_bounds_update", "vx_score_topk_bounds",
                  "vx_sparse_paged_decode",
-                 "vx_full_paged_decode", "vx_sparse_decode_step", "vx_decode_layers",
+                 "vx_full_paged_decode", "vx_sparse_decode_step", "vx_sparse_decode_step_bounds",
+                 "vx_decode_layers",
                  "vx_workspace_size", "vx_set_pages_per_split", "vx_version"):
         getattr(lib, name).restype = I32
     _lib = lib
@@ -320,6 +324,16 @@ def sparse_decode_step(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_
                                sel, out, lse, workspace, stream)()
 
 
+def sparse_decode_step_bounds(kv: PagedKV, batch: Batch, bounds: torch.Tensor, q: torch.Tensor,
+                              topk: int, n_bos: int, n_eos: int, update_completed: bool,
+                              sm_scale: float, sel: torch.Tensor, out: torch.Tensor,
+                              lse: Optional[torch.Tensor], workspace: torch.Tensor, stream=None):
+    """vx_sparse_decode_step_bounds: the decode step under Quest's key-bounds
+    rule (completed pages' bounds, selection and attention)."""
+    prepare_sparse_decode_step_bounds(kv, batch, bounds, q, topk, n_bos, n_eos, update_completed,
+                                      sm_scale, sel, out, lse, workspace, stream)()
+
+
 def set_pages_per_split(n: int):
     """Test hook: force the decode split size (0 = planner)."""
     _check(load_library().vx_set_pages_per_split(int(n)), "vx_set_pages_per_split")
@@ -416,6 +430,22 @@ def prepare_sparse_decode_step(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos,
             _ptr(workspace), workspace.numel(), _stream(stream))
     return PreparedCall(lib.vx_sparse_decode_step, args, "vx_sparse_decode_step",
                         (kvs, bs, kv, batch, q, sel, out, lse, workspace))
+
+
+def prepare_sparse_decode_step_bounds(kv: PagedKV, batch: Batch, bounds, q, topk, n_bos, n_eos,
+                                      update_completed, sm_scale, sel, out, lse, workspace,
+                                      stream=None) -> PreparedCall:
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    _need(out, "out")
+    _need(bounds, "bounds", kv.k_cache.dtype)
+    kvs, bs = kv.struct(), batch.struct()
+    lib = load_library()
+    args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(bounds), _ptr(q), topk, n_bos, n_eos,
+            1 if update_completed else 0, float(sm_scale), _ptr(sel), _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    return PreparedCall(lib.vx_sparse_decode_step_bounds, args, "vx_sparse_decode_step_bounds",
+                        (kvs, bs, kv, batch, bounds, q, sel, out, lse, workspace))
 
 
 def prepare_decode_layers(kvs: list, batch: Batch, qs: list, dense: Optional[list], topk: int,

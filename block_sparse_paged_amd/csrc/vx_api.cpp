@@ -339,6 +339,24 @@ hipError_t launch_completed_centroids(const vx_paged_kv* kv, const vx_batch* bat
   return launch_centroid(kv->dtype, c, stream);
 }
 
+// The bounds kernel over the page each request's latest token completed.
+hipError_t launch_completed_bounds(const vx_paged_kv* kv, const vx_batch* batch, void* bounds,
+                                   hipStream_t stream) {
+  BoundsArgs a{};
+  a.k = kv->k_cache;
+  a.bounds = bounds;
+  a.ids = nullptr;
+  a.pt = batch->page_table;
+  a.seq_lens = batch->seq_lens;
+  a.n_ids = batch->batch;
+  a.H_kv = kv->num_kv_heads;
+  a.S_p = kv->page_size;
+  a.D = kv->head_dim_qk;
+  a.pt_stride = batch->max_pages_per_req;
+  a.max_tokens = batch->max_seq_len;
+  return launch_page_bounds(kv->dtype, a, stream);
+}
+
 // The split indexer's scoring kernel alone: fp32 scores [B, H_kv, mp] into
 // `scores`.  With update_completed it also writes the completed pages'
 // centroids (in the kernel when each block's share of a page fits, else with
@@ -392,6 +410,33 @@ hipError_t launch_split_score(const vx_paged_kv* kv, const vx_batch* batch, cons
   }
 }
 
+// The split scorer of the bound rule: fp32 scores [B, H_kv, mp] into `scores`.
+hipError_t launch_split_bound_score(const vx_paged_kv* kv, const vx_batch* batch,
+                                    const void* bounds, const void* q, int32_t n_bos,
+                                    int32_t n_eos, float* scores, hipStream_t stream) {
+  const int mp = max_pages_eff(kv, batch);
+  const int max_cand = std::max(mp - n_bos - n_eos, 0);
+  ScoreArgs s{};
+  s.q = q;
+  s.cent = bounds;
+  s.pt = batch->page_table;
+  s.seq_lens = batch->seq_lens;
+  s.scores = scores;
+  s.B = batch->batch;
+  s.H_q = batch->num_q_heads;
+  s.H_kv = kv->num_kv_heads;
+  s.D = kv->head_dim_qk;
+  s.S_p = kv->page_size;
+  s.pt_stride = batch->max_pages_per_req;
+  s.score_stride = mp;
+  s.max_tokens = batch->max_seq_len;
+  s.n_bos = n_bos;
+  s.n_eos = n_eos;
+  const int cpb = split_score_chunk(batch, max_cand);
+  s.cand_per_block = cpb;
+  return launch_bound_score(kv->dtype, s, ceil_div(max_cand, cpb), stream);
+}
+
 size_t step_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
   // the indexer's scores and the decode partials side by side (the decode
   // kernel may select from the scores while it writes partials)
@@ -408,10 +453,10 @@ size_t attention_lds_bytes(int D, int G) {
   return std::max(att_valu, att_mfma);
 }
 
-size_t step_lds_bytes(int max_pages, int k_tot, int D, int G, int ordered_batch) {
+size_t step_lds_bytes(int max_pages, int k_tot, int D, int G, int ordered_batch, bool bounds) {
   const size_t dyn = step_dynamic_lds(max_pages, k_tot, ordered_batch);
   const size_t stat = (size_t)D * 4 + kSelectLdsBytes + attention_lds_bytes(D, G) +
-                      16 * (size_t)D * 4 + 16;
+                      (bounds ? 32 : 16) * (size_t)D * 4 + 16;
   return dyn + stat;
 }
 
@@ -434,10 +479,11 @@ vx_status full_decode_check(const vx_paged_kv* kv, const vx_batch* batch, const 
   return VX_OK;
 }
 
-vx_status step_check(const vx_paged_kv* kv, const vx_batch* batch, const void* q, int32_t topk,
-                     int32_t n_bos, int32_t n_eos, int32_t update_completed, float sm_scale,
-                     const int32_t* sel, const void* out, const void* workspace,
-                     size_t workspace_bytes) {
+// summary: the centroid table, or the key-bounds table of the bound rule.
+vx_status step_check(const vx_paged_kv* kv, const vx_batch* batch, const void* summary,
+                     const void* q, int32_t topk, int32_t n_bos, int32_t n_eos,
+                     int32_t update_completed, float sm_scale, const int32_t* sel,
+                     const void* out, const void* workspace, size_t workspace_bytes) {
   vx_status st = check_kv(kv);
   if (st != VX_OK) return st;
   if ((st = check_batch(kv, batch)) != VX_OK) return st;
@@ -447,7 +493,7 @@ vx_status step_check(const vx_paged_kv* kv, const vx_batch* batch, const void* q
   if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
   if (batch->batch == 0) return VX_OK;
   if (!q || !sel || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) ||
-      !kv->centroids || !batch->page_table || !batch->seq_lens)
+      !summary || !batch->page_table || !batch->seq_lens)
     return VX_ERR_INVALID_ARGUMENT;
   if (max_pages_eff(kv, batch) > kMaxCandidates) return VX_ERR_UNSUPPORTED;
   if (workspace_bytes < step_ws_bytes(kv, batch, topk + n_bos + n_eos))
@@ -608,28 +654,9 @@ vx_status vx_score_topk_bounds(const vx_paged_kv* kv, const vx_batch* batch, con
     s.scores = scores;     // not read by the fused kernel
     return hip_status(launch_indexer_fused(kv->dtype, s, t, stream, true));
   }
-  if (need_scores) {
-    ScoreArgs s{};
-    s.q = q;
-    s.cent = bounds;
-    s.pt = batch->page_table;
-    s.seq_lens = batch->seq_lens;
-    s.scores = scores;
-    s.B = batch->batch;
-    s.H_q = batch->num_q_heads;
-    s.H_kv = kv->num_kv_heads;
-    s.D = kv->head_dim_qk;
-    s.S_p = kv->page_size;
-    s.pt_stride = batch->max_pages_per_req;
-    s.score_stride = mp;
-    s.max_tokens = batch->max_seq_len;
-    s.n_bos = n_bos;
-    s.n_eos = n_eos;
-    const int cpb = split_score_chunk(batch, max_cand);
-    s.cand_per_block = cpb;
-    if (launch_bound_score(kv->dtype, s, ceil_div(max_cand, cpb), stream) != hipSuccess)
-      return VX_ERR_HIP;
-  }
+  if (need_scores &&
+      launch_split_bound_score(kv, batch, bounds, q, n_bos, n_eos, scores, stream) != hipSuccess)
+    return VX_ERR_HIP;
   return hip_status(launch_topk(t, need_scores ? max_cand : 0, stream));
 }
 
@@ -681,14 +708,22 @@ vx_status vx_full_paged_decode(const vx_paged_kv* kv, const vx_batch* batch, con
                     stream);
 }
 
-vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
-                                int32_t topk, int32_t n_bos, int32_t n_eos,
-                                int32_t update_completed, float sm_scale, int32_t* sel,
-                                void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
-  vx_status st = step_check(kv, batch, q, topk, n_bos, n_eos, update_completed, sm_scale, sel,
-                            out, workspace, workspace_bytes);
+}  // extern "C"
+
+namespace {
+
+// One decode step under the centroid rule or the bound rule (bounds: the
+// key-bounds table [P, H_kv, 2, D]).
+vx_status decode_step_impl(const vx_paged_kv* kv, const vx_batch* batch, bool use_bounds,
+                           void* bounds, const void* q, int32_t topk, int32_t n_bos,
+                           int32_t n_eos, int32_t update_completed, float sm_scale, int32_t* sel,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  void* summary = use_bounds ? bounds : kv->centroids;
+  vx_status st = step_check(kv, batch, summary, q, topk, n_bos, n_eos, update_completed, sm_scale,
+                            sel, out, workspace, workspace_bytes);
   if (st != VX_OK || batch->batch == 0) return st;
+  if (use_bounds && is_mla(kv)) return VX_ERR_UNSUPPORTED;
   const int mp = max_pages_eff(kv, batch);
   const int k_tot = topk + n_bos + n_eos;
   const int G = batch->num_q_heads / kv->num_kv_heads;
@@ -703,7 +738,7 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
   const int ordered = (waves == 4 && batch->batch <= kMaxOrderedBatch) ? batch->batch : 0;
   if (!is_mla(kv) && decode_step_supported(kv->dtype, kv->head_dim_qk, G) &&
       (units >= kNumCUs / 2 || units * mp <= 4096) &&
-      step_lds_bytes(mp, k_tot, kv->head_dim_qk, G, ordered) <= max_lds_per_block()) {
+      step_lds_bytes(mp, k_tot, kv->head_dim_qk, G, ordered, use_bounds) <= max_lds_per_block()) {
     StepArgs a{};
     DecodeArgs& d = a.d;
     d.q = q;
@@ -726,7 +761,7 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
     d.lse = lse;
     ScoreArgs& sc = a.s;
     sc.q = q;
-    sc.cent = kv->centroids;
+    sc.cent = summary;
     sc.pt = batch->page_table;
     sc.seq_lens = batch->seq_lens;
     sc.scores = reinterpret_cast<float*>(workspace);   // not read by the fused kernel
@@ -741,7 +776,7 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
     sc.n_bos = n_bos;
     sc.n_eos = n_eos;
     a.sel = sel;
-    a.cent = kv->centroids;
+    a.cent = summary;
     a.topk = topk;
     a.n_bos = n_bos;
     a.n_eos = n_eos;
@@ -749,8 +784,10 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
     a.max_pages = mp;
     a.update_completed = update_completed;
     a.longest_first = ordered > 0;
-    return hip_status(launch_decode_step(kv->dtype, kv->head_dim_qk, G, waves, a, stream));
+    return hip_status(
+        launch_decode_step(kv->dtype, kv->head_dim_qk, G, waves, a, stream, use_bounds));
   }
+
 
   // Otherwise: the indexer (with the completed pages' centroids), then
   // attention.
@@ -765,6 +802,25 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
                          attention_lds_bytes(kv->head_dim_qk, G);
   const bool select_fits = is_mla(kv) ? mla_select_fits(mp, k_tot)
                                       : sel_lds <= max_lds_per_block();
+  if (use_bounds) {
+    // the completed pages' bounds first: the bound indexers do not write them
+    if (update_completed && launch_completed_bounds(kv, batch, bounds, stream) != hipSuccess)
+      return VX_ERR_HIP;
+    if (split_scorer && max_cand > topk && topk > 0 && select_fits) {
+      float* scores = reinterpret_cast<float*>(workspace);
+      if (launch_split_bound_score(kv, batch, bounds, q, n_bos, n_eos, scores, stream) !=
+          hipSuccess)
+        return VX_ERR_HIP;
+      SelectInDecode fs{scores, sel, mp, topk, n_bos, n_eos, align_up(score_ws_bytes(kv, batch))};
+      return run_decode(kv, batch, q, nullptr, k_tot, sm_scale, out, lse, workspace,
+                        workspace_bytes, stream, &fs);
+    }
+    st = vx_score_topk_bounds(kv, batch, bounds, q, topk, n_bos, n_eos, sel, workspace,
+                              workspace_bytes, stream);
+    if (st != VX_OK) return st;
+    return run_decode(kv, batch, q, sel, k_tot, sm_scale, out, lse, workspace, workspace_bytes,
+                      stream);
+  }
   if (split_scorer && max_cand > topk && topk > 0 && select_fits) {
     float* scores = reinterpret_cast<float*>(workspace);
     if (launch_split_score(kv, batch, q, n_bos, n_eos, scores, update_completed != 0, stream) !=
@@ -779,6 +835,28 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
   if (st != VX_OK) return st;
   return run_decode(kv, batch, q, sel, k_tot, sm_scale, out, lse, workspace, workspace_bytes,
                     stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                                int32_t topk, int32_t n_bos, int32_t n_eos,
+                                int32_t update_completed, float sm_scale, int32_t* sel,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return decode_step_impl(kv, batch, false, nullptr, q, topk, n_bos, n_eos, update_completed, sm_scale,
+                          sel, out, lse, workspace, workspace_bytes, stream);
+}
+
+vx_status vx_sparse_decode_step_bounds(const vx_paged_kv* kv, const vx_batch* batch,
+                                       void* bounds, const void* q, int32_t topk, int32_t n_bos,
+                                       int32_t n_eos, int32_t update_completed, float sm_scale,
+                                       int32_t* sel, void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  return decode_step_impl(kv, batch, true, bounds, q, topk, n_bos, n_eos, update_completed, sm_scale,
+                          sel, out, lse, workspace, workspace_bytes, stream);
 }
 
 vx_status vx_decode_layers(const vx_paged_kv* kv, const vx_batch* batch, const void* const* q,
@@ -798,8 +876,8 @@ vx_status vx_decode_layers(const vx_paged_kv* kv, const vx_batch* batch, const v
       st = full_decode_check(&kv[l], batch, q[l], sm_scale, out[l], workspace, workspace_bytes);
     } else {
       if (!sel) return VX_ERR_INVALID_ARGUMENT;
-      st = step_check(&kv[l], batch, q[l], topk, n_bos, n_eos, update_completed, sm_scale, sel[l],
-                      out[l], workspace, workspace_bytes);
+      st = step_check(&kv[l], batch, kv[l].centroids, q[l], topk, n_bos, n_eos, update_completed,
+                      sm_scale, sel[l], out[l], workspace, workspace_bytes);
     }
     if (st != VX_OK) return st;
   }

@@ -107,6 +107,69 @@ struct TileCentroid {
   }
 };
 
+// The key bounds of one page-head tile (per-channel minimum and maximum,
+// Quest's page summary) inside a longer kernel, with TileCentroid's row
+// layout and load(): reduce() keeps each row group's minimum and maximum in
+// LDS `red` [2][RG][D], finish() takes them over the groups for segment t
+// and stores the two rows (minimum first).  Minimum and maximum are exact,
+// so the rows equal the bounds kernel's in any order (but for the sign of a
+// zero that ties with another zero).
+template <typename T, int D, int NT>
+struct TileBounds : TileCentroid<T, D, NT> {
+  using Base = TileCentroid<T, D, NT>;
+  using S = typename Base::S;
+
+  __device__ __forceinline__ void reduce(float* red, int S_p) const {
+#pragma unroll
+    for (int c = 0; c < Base::CP; ++c) {
+      const int pr = threadIdx.x + c * NT, g = pr / S::SEGS, sg = pr % S::SEGS;
+      if (pr < S::THREADS) {
+        float lo[S::E], hi[S::E];
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) {
+          lo[e] = INFINITY;
+          hi[e] = -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < Base::CR; ++j) {
+          if (g + j * S::RG < S_p) {
+            float f[S::E];
+            Vec16<T>::unpack(this->rows[c][j], f);
+#pragma unroll
+            for (int e = 0; e < S::E; ++e) {
+              lo[e] = fminf(lo[e], f[e]);
+              hi[e] = fmaxf(hi[e], f[e]);
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) {
+          red[g * D + sg * S::E + e] = lo[e];
+          red[(S::RG + g) * D + sg * S::E + e] = hi[e];
+        }
+      }
+    }
+  }
+
+  // bounds_row: the page-head's two summary rows [2][D]
+  static __device__ __forceinline__ void finish(const float* red, int, T* bounds_row, int t) {
+    float lo[S::E], hi[S::E];
+#pragma unroll
+    for (int e = 0; e < S::E; ++e) {
+      lo[e] = INFINITY;
+      hi[e] = -INFINITY;
+    }
+    for (int g = 0; g < S::RG; ++g)
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) {
+        lo[e] = fminf(lo[e], red[g * D + t * S::E + e]);
+        hi[e] = fmaxf(hi[e], red[(S::RG + g) * D + t * S::E + e]);
+      }
+    st16(bounds_row + t * S::E, Vec16<T>::pack(lo));
+    st16(bounds_row + D + t * S::E, Vec16<T>::pack(hi));
+  }
+};
+
 // Part of the centroid rows of one page computed inside a longer kernel of NT
 // threads, again in the centroid kernel's order: the block takes units
 // [u0, u0 + nu) of the page's (KV head, 16-byte segment) pairs (unit u: head

@@ -132,8 +132,12 @@ hipError_t launch_topk(const TopkArgs& a, int max_cand, hipStream_t s);
 struct BoundsArgs {
   const void* k;          // [P, H_kv, S_p, D]
   void* bounds;           // [P, H_kv, 2, D]
-  const int32_t* ids;     // [n_ids] physical pages
+  const int32_t* ids;     // [n_ids] physical pages, or nullptr: one block per request,
+                          // for the page its latest token completed (if any)
+  const int32_t* pt;      // [B, pt_stride] (ids == nullptr)
+  const int32_t* seq_lens;
   int32_t n_ids, H_kv, S_p, D;
+  int32_t pt_stride, max_tokens;
 };
 hipError_t launch_page_bounds(int dtype, const BoundsArgs& a, hipStream_t s);
 hipError_t launch_bound_score(int dtype, const ScoreArgs& a, int grid_x, hipStream_t s);
@@ -156,8 +160,9 @@ constexpr int round4(int n) { return (n + 3) & ~3; }
 // Dynamic LDS bytes of a fused step block; ordered_batch = B when block rows
 // go to requests longest first, else 0.
 size_t step_dynamic_lds(int max_pages, int k_tot, int ordered_batch);
-// waves: 4 or 8 per block (one block per (request, KV head)).
+// waves: 4 or 8 per block (one block per (request, KV head)).  bounds: the
+// key-bounds rule (a.s.cent and a.cent are the key-bounds table).
 hipError_t launch_decode_step(int dtype, int D, int G, int waves, const StepArgs& a,
-                              hipStream_t s);
+                              hipStream_t s, bool bounds = false);
 
 }  // namespace vx

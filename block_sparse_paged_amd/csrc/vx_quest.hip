@@ -8,7 +8,8 @@
 // pipeline's (K3, K4, K5); only the summary and the scores differ.  As for
 // the centroids, q is the group mean of a KV head's query heads.
 //
-// K8 bounds_kernel: one block per listed page; thread (KV head, 16-byte
+// K8 bounds_kernel: one block per listed page (or per request, for the page
+//    its latest token completed); thread (KV head, 16-byte
 //    segment) pairs read the page's rows, 16 loads in flight, keep the
 //    channel minimum and maximum in fp32 (exact: both are key values) and
 //    write them as two rows in the KV dtype.  Summary layout [P, H_kv, 2, D],
@@ -34,7 +35,15 @@ template <typename T, int D>
 __global__ __launch_bounds__(kBoundsThreads) void bounds_kernel(BoundsArgs a) {
   using V = Vec16<T>;
   constexpr int E = V::E, SEGS = D / E;
-  const int page = a.ids[blockIdx.x];
+  int page;
+  if (a.ids) {
+    page = a.ids[blockIdx.x];
+  } else {                                   // request blockIdx.x's completed page, if any
+    int L = a.seq_lens[blockIdx.x];
+    L = L < 0 ? 0 : (L > a.max_tokens ? a.max_tokens : L);
+    if (L == 0 || L % a.S_p != 0) return;
+    page = a.pt[(size_t)blockIdx.x * a.pt_stride + L / a.S_p - 1];
+  }
   const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)page * a.H_kv * a.S_p * D;
   T* bp = reinterpret_cast<T*>(a.bounds) + (size_t)page * a.H_kv * 2 * D;
   for (int i = threadIdx.x; i < a.H_kv * SEGS; i += kBoundsThreads) {

@@ -31,6 +31,8 @@
 // the blocks take several rounds of the GPU, rows of blocks go to requests
 // longest first (blocks start in about linear order), so that the long
 // requests of a mixed batch do not start last and run alone at the end.
+#include <type_traits>
+
 #include "vx_attend.h"
 #include "vx_centroid.h"
 #include "vx_select.h"
@@ -69,13 +71,17 @@ __device__ __forceinline__ int longest_first_request(const int32_t* seq_lens, in
   return *pick;
 }
 
-template <typename T, int D, int G, int HS, int PF, int NW>
+// BOUNDS: the second summary rule (Quest's key bounds): the summary table
+// holds two rows per (page, head), candidates are scored by the bound, and
+// the completed page gets its bounds instead of its centroid.
+template <typename T, int D, int G, int HS, int PF, int NW, bool BOUNDS>
 __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   constexpr int NT = NW * 64;
   extern __shared__ __align__(16) uint32_t dyn[];   // page row, keys (each round4(max_pages)), list [k_tot]
   __shared__ float qbar[D];
   __shared__ SelectLds<NT> sl;
-  __shared__ float cred[CentroidShape<T, D>::RG][D];     // completed page: row-group sums
+  // completed page: row-group sums (bounds: minima, then maxima)
+  __shared__ float cred[(BOUNDS ? 2 : 1) * CentroidShape<T, D>::RG][D];
 
   __shared__ int pick;
 
@@ -120,12 +126,13 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
   // The page this step's token completed: its K tile rows are loaded now and
   // summed per row group after the scoring loop (the loads complete under
   // the scoring's), the groups are added at the end.
-  using TC = TileCentroid<T, D, NT>;
+  using TC = std::conditional_t<BOUNDS, TileBounds<T, D, NT>, TileCentroid<T, D, NT>>;
+  constexpr int RS = BOUNDS ? 2 : 1;           // summary rows per (page, head)
   const bool upd = a.update_completed && seq > 0 && seq % SP == 0;
   TC tc;
   if (upd) tc.load(reinterpret_cast<const T*>(a.d.k) + ((size_t)prow[n_b - 1] * s.H_kv + h) * SP * D, SP);
 
-  if (scoring) score_head<T, D, NT>(s, h, n_cand, prow + a.n_bos, qbar, keys, sl);
+  if (scoring) score_head<T, D, NT, BOUNDS>(s, h, n_cand, prow + a.n_bos, qbar, keys, sl);
   if (upd) tc.reduce(&cred[0][0], SP);
   const int count = select_pages<NT>(keys, n_cand, n_b, a.topk, a.n_bos, a.n_eos, a.k_tot,
                                      nullptr, list, sl);
@@ -146,32 +153,33 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
     for (int i = t; i < a.k_tot; i += nt) srow[i] = i < count ? list[i] : -1;
     if (upd && t < TC::S::SEGS)
       TC::finish(&cred[0][0], SP,
-                 reinterpret_cast<T*>(a.cent) + ((size_t)prow[n_b - 1] * s.H_kv + h) * D, t);
+                 reinterpret_cast<T*>(a.cent) + ((size_t)prow[n_b - 1] * s.H_kv + h) * RS * D, t);
   };
   attend_pages<T, D, G, HS, PF, NW>(a.d, b, h, 0, 0, count, seq, page_at, epilogue);
 }
 
-template <typename T, int D, int G, int NW>
+template <typename T, int D, int G, int NW, bool BOUNDS>
 hipError_t run_step(const StepArgs& a, hipStream_t s) {
   constexpr int HS = attend_head_slices<G>(), PF = attend_prefetch<T, D>();
   const size_t lds = step_dynamic_lds(a.max_pages, a.k_tot, a.longest_first ? a.s.B : 0);
-  hipLaunchKernelGGL((decode_step_kernel<T, D, G, HS, PF, NW>), dim3(a.s.H_kv, a.s.B),
+  hipLaunchKernelGGL((decode_step_kernel<T, D, G, HS, PF, NW, BOUNDS>), dim3(a.s.H_kv, a.s.B),
                      dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
 template <typename T, int D, int G>
-hipError_t run_step_w(int waves, const StepArgs& a, hipStream_t s) {
-  return waves == 4 ? run_step<T, D, G, 4>(a, s) : run_step<T, D, G, 8>(a, s);
+hipError_t run_step_w(int waves, bool bounds, const StepArgs& a, hipStream_t s) {
+  if (bounds) return waves == 4 ? run_step<T, D, G, 4, true>(a, s) : run_step<T, D, G, 8, true>(a, s);
+  return waves == 4 ? run_step<T, D, G, 4, false>(a, s) : run_step<T, D, G, 8, false>(a, s);
 }
 
 template <typename T, int D>
-hipError_t run_step_g(int G, int waves, const StepArgs& a, hipStream_t s) {
+hipError_t run_step_g(int G, int waves, bool bounds, const StepArgs& a, hipStream_t s) {
   switch (G) {
-    case 1: return run_step_w<T, D, 1>(waves, a, s);
-    case 2: return run_step_w<T, D, 2>(waves, a, s);
-    case 4: return run_step_w<T, D, 4>(waves, a, s);
-    case 8: return run_step_w<T, D, 8>(waves, a, s);
+    case 1: return run_step_w<T, D, 1>(waves, bounds, a, s);
+    case 2: return run_step_w<T, D, 2>(waves, bounds, a, s);
+    case 4: return run_step_w<T, D, 4>(waves, bounds, a, s);
+    case 8: return run_step_w<T, D, 8>(waves, bounds, a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -190,14 +198,14 @@ bool decode_step_supported(int dtype, int D, int G) {
 }
 
 hipError_t launch_decode_step(int dtype, int D, int G, int waves, const StepArgs& a,
-                              hipStream_t s) {
+                              hipStream_t s, bool bounds) {
   if (waves != 4 && waves != 8) return hipErrorInvalidValue;
   if (dtype == 0) {
-    if (D == 64) return run_step_g<float, 64>(G, waves, a, s);
-    if (D == 128) return run_step_g<float, 128>(G, waves, a, s);
+    if (D == 64) return run_step_g<float, 64>(G, waves, bounds, a, s);
+    if (D == 128) return run_step_g<float, 128>(G, waves, bounds, a, s);
   } else {
-    if (D == 64) return run_step_g<bf16_t, 64>(G, waves, a, s);
-    if (D == 128) return run_step_g<bf16_t, 128>(G, waves, a, s);
+    if (D == 64) return run_step_g<bf16_t, 64>(G, waves, bounds, a, s);
+    if (D == 128) return run_step_g<bf16_t, 128>(G, waves, bounds, a, s);
   }
   return hipErrorInvalidValue;
 }

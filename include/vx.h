@@ -20,7 +20,7 @@
  * a step in one capturable call (vx_decode_layers), the write path with
  * centroids on completion (vx_append_kv), the lossy radix indexer
  * (vx_score_topk_radix) and a second summary rule, Quest's key bounds
- * (vx_bounds_update, vx_score_topk_bounds).
+ * (vx_bounds_update, vx_score_topk_bounds, vx_sparse_decode_step_bounds).
  *
  * Conventions shared by every call
  *   Pointers.   Every buffer pointer is a DEVICE pointer unless marked
@@ -294,6 +294,25 @@ vx_status vx_sparse_decode_step(const vx_paged_kv* kv, const vx_batch* batch, co
                                 int32_t update_completed, float sm_scale, int32_t* sel,
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/* vx_sparse_decode_step under the key-bounds rule (Quest, section 3, as
+ * for vx_score_topk_bounds above).  Equivalent to, in order:
+ *   - when update_completed == 1, vx_bounds_update on the page each
+ *     request's newest token completed;
+ *   - vx_score_topk_bounds(kv, batch, bounds, q, topk, n_bos, n_eos, sel, ...);
+ *   - vx_sparse_paged_decode(kv, batch, q, sel, topk + n_bos + n_eos, ...).
+ * kv->centroids is not read.  Dispatch (one fused kernel or separate
+ * launches), exactness and workspace (VX_OP_DECODE_STEP's size) as for
+ * vx_sparse_decode_step; the bounds rows equal vx_bounds_update's (up to
+ * the sign of a zero minimum or maximum that ties with another zero).
+ *   bounds     device [P, H_kv, 2, D_qk], dtype (read; the completed pages'
+ *              rows written)
+ * D_qk in {64, 128}; MLA shapes return VX_ERR_UNSUPPORTED. */
+vx_status vx_sparse_decode_step_bounds(const vx_paged_kv* kv, const vx_batch* batch,
+                                       void* bounds, const void* q, int32_t topk, int32_t n_bos,
+                                       int32_t n_eos, int32_t update_completed, float sm_scale,
+                                       int32_t* sel, void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 /* The attention layers of one decode step in one call (README, "Using
  * Your Sparse Attention with SGLang": with sparsity on, the layers listed as

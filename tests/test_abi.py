@@ -338,3 +338,35 @@ def test_bounds_arguments_rejected(lib):
                  None) == vx.VX_ERR_UNSUPPORTED
     assert score(r(kv), r(batch_struct(batch=0)), None, None, 30, 1, 1, None, None, 0,
                  None) == vx.VX_OK
+
+
+def test_step_bounds_arguments_rejected(lib):
+    """vx_sparse_decode_step_bounds checks as vx_sparse_decode_step, with the
+    bounds table in place of the centroid table (which it does not read)."""
+    r = ctypes.byref
+    step = lib.vx_sparse_decode_step_bounds
+    kv, bt = kv_struct(), batch_struct()
+    need = ws_size(lib, vx.VX_OP_DECODE_STEP, kv, bt, 32)[1]
+    good = dict(bounds=FAKE, q=FAKE, topk=30, bos=1, eos=1, upd=1, scale=0.1, sel=FAKE, out=FAKE,
+                ws=FAKE, ws_bytes=need)
+
+    def call(kv=kv, bt=bt, **kw):
+        a = dict(good, **kw)
+        return step(r(kv), r(bt), a["bounds"], a["q"], a["topk"], a["bos"], a["eos"], a["upd"],
+                    a["scale"], a["sel"], a["out"], None, a["ws"], a["ws_bytes"], None)
+
+    assert call(bounds=None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(q=None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(eos=0) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(upd=2) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(scale=0.0) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(ws_bytes=need - 1) == vx.VX_ERR_WORKSPACE_TOO_SMALL
+    assert call(bt=batch_struct(max_pages_per_req=20000, max_seq_len=16 * 20000),
+                ws_bytes=1 << 40) == vx.VX_ERR_UNSUPPORTED        # more pages than it selects from
+    mla = kv_struct(head_dim_qk=576, head_dim_v=512, num_kv_heads=1, page_size=64,
+                    v_aliases_k=1, v_cache=None)
+    assert call(kv=mla, bt=batch_struct(num_q_heads=32, max_seq_len=64 * 64),
+                ws_bytes=1 << 40) == vx.VX_ERR_UNSUPPORTED
+    assert call(kv=kv_struct(centroids=None), bounds=None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert call(bt=batch_struct(batch=0), bounds=None, q=None, sel=None, out=None,
+                ws=None) == vx.VX_OK
