@@ -10,8 +10,9 @@
 //      stored at the end);
 //   4. attend over the selected pages (K/V loads start as soon as the list
 //      exists: physical pages come from the staged row, no HBM round trip);
-//   5. if the token completed a page, write that page's centroid row for
-//      this head (the page is the last, reserved one, so no score of this
+//   5. if the token completed a page, write that page's centroid row (key
+//      bounds: its minimum and maximum rows) for this head (the page is
+//      the last, reserved one, so no score of this
 //      step reads it).  Its K tile is loaded before the scoring loop and
 //      reduced per row group after it, so the loads cost no extra round
 //      trip; the row groups are added at the end.
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepArgs a) {
     }
     return make_int2(logi, phys);
   };
-  // the row of `sel` and the completed page's centroid, by threads the
+  // the row of `sel` and the completed page's summary rows, by threads the
   // attention's merge leaves idle (stored late, so no barrier waits on them)
   int32_t* srow = a.sel + ((size_t)b * s.H_kv + h) * a.k_tot;
   auto epilogue = [&](int t, int nt) {
