@@ -36,8 +36,8 @@ EXPORTS = ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk
            "vx_bounds_update", "vx_score_topk_bounds",
            "vx_sparse_paged_decode",
            "vx_full_paged_decode", "vx_sparse_decode_step", "vx_sparse_decode_step_bounds",
-           "vx_decode_layers",
-           "vx_workspace_size", "vx_set_pages_per_split", "vx_status_string", "vx_version")
+           "vx_decode_layers", "vx_plan_decode", "vx_paged_decode_planned",
+           "vx_workspace_size", "vx_status_string", "vx_version")
 
 
 class VxError(RuntimeError):
@@ -54,6 +54,14 @@ class PagedKVStruct(ctypes.Structure):
         ("v_aliases_k", ctypes.c_int32), ("reserved_", ctypes.c_int32),
         ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
         ("centroids", ctypes.c_void_p),
+    ]
+
+
+class DecodePlanStruct(ctypes.Structure):
+    _fields_ = [
+        ("op", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+        ("pages_per_split", ctypes.c_int32), ("n_split", ctypes.c_int32),
+        ("reserved_", ctypes.c_int32 * 2), ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -95,7 +103,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_decode_layers.argtypes = [kvp, btp, VP, I32, VP, I32, I32, I32, I32, F32, VP, VP, VP,
                                      VP, SZ, VP]
     lib.vx_workspace_size.argtypes = [I32, kvp, btp, I32, P(SZ)]
-    lib.vx_set_pages_per_split.argtypes = [I32]
+    lib.vx_plan_decode.argtypes = [I32, kvp, btp, I32, I32, I32, P(DecodePlanStruct)]
+    lib.vx_paged_decode_planned.argtypes = [kvp, btp, VP, VP, I32, P(DecodePlanStruct), F32, VP,
+                                            VP, VP, SZ, VP]
     lib.vx_status_string.argtypes = [I32]
     lib.vx_status_string.restype = ctypes.c_char_p
     lib.vx_version.argtypes = []
@@ -103,8 +113,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                  "vx_bounds_update", "vx_score_topk_bounds",
                  "vx_sparse_paged_decode",
                  "vx_full_paged_decode", "vx_sparse_decode_step", "vx_sparse_decode_step_bounds",
-                 "vx_decode_layers",
-                 "vx_workspace_size", "vx_set_pages_per_split", "vx_version"):
+                 "vx_decode_layers", "vx_plan_decode", "vx_paged_decode_planned",
+                 "vx_workspace_size", "vx_version"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -334,9 +344,33 @@ def sparse_decode_step_bounds(kv: PagedKV, batch: Batch, bounds: torch.Tensor, q
                                       sm_scale, sel, out, lse, workspace, stream)()
 
 
-def set_pages_per_split(n: int):
-    """Test hook: force the decode split size (0 = planner)."""
-    _check(load_library().vx_set_pages_per_split(int(n)), "vx_set_pages_per_split")
+def plan_decode(op: int, kv: PagedKV, batch: Batch, k_tot: int = 0, num_cus: int = 0,
+                pages_per_split: int = 0) -> DecodePlanStruct:
+    """vx_plan_decode: the launch plan of a sparse (VX_OP_SPARSE_DECODE) or
+    dense (VX_OP_FULL_DECODE) decode call on a GPU of ``num_cus`` compute
+    units (0: the current device), optionally with a fixed split size."""
+    plan = DecodePlanStruct()
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_plan_decode(op, ctypes.byref(kvs), ctypes.byref(bs), int(k_tot),
+                                         int(num_cus), int(pages_per_split), ctypes.byref(plan)),
+           "vx_plan_decode")
+    return plan
+
+
+def paged_decode_planned(kv: PagedKV, batch: Batch, q: torch.Tensor, sel: Optional[torch.Tensor],
+                         plan: DecodePlanStruct, sm_scale: float, out: torch.Tensor,
+                         lse: Optional[torch.Tensor], workspace: torch.Tensor, stream=None):
+    """vx_paged_decode_planned: the sparse (sel given) or dense (sel None)
+    decode with an explicit plan from plan_decode."""
+    _need(q, "q")
+    _need(out, "out")
+    if sel is not None:
+        _need(sel, "sel", torch.int32)
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_paged_decode_planned(
+        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), _ptr(sel),
+        0 if sel is None else sel.shape[-1], ctypes.byref(plan), float(sm_scale), _ptr(out),
+        _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)), "vx_paged_decode_planned")
 
 
 def version() -> int:

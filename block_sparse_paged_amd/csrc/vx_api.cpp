@@ -2,13 +2,11 @@
 // launch planning, workspace layout and kernel dispatch.
 //
 // Planning ("workload planner for balanced GPU scheduling", Vortex article,
-// "A dual-stage programmable abstraction") is a pure function of the shapes:
-// every (request, KV head) is cut into splits of whole pages so that the
-// launch holds enough waves to keep all 256 CUs of an MI355X streaming, and
-// the fp32 partials the splits produce stay a small fraction of the K/V
-// bytes they replace.  Splits that fall beyond a short request's pages exit
-// at once, which keeps heterogeneous batches balanced without a device-side
-// work list.
+// "A dual-stage programmable abstraction") is a pure function of the shapes
+// and of the GPU's compute-unit count (queried once per device): every
+// (request, KV head) is cut into splits of whole pages so that the launch
+// holds enough waves to keep every CU streaming, and the fp32 partials the
+// splits produce stay a small fraction of the K/V bytes they replace.
 #include <stddef.h>
 #include <stdint.h>
 
@@ -21,42 +19,58 @@ namespace {
 
 using namespace vx;
 
-constexpr int kNumCUs = 256;                    // MI355X
-// blocks per launch the planner aims for (split decode blocks are 8 waves,
-// MLA blocks 4): one wave of resident blocks for the sparse step, several
-// for the long dense stream so that unequal requests even out
-constexpr int kSparseTargetBlocks = kNumCUs;
-constexpr int kFullTargetBlocks = kNumCUs * 16;
+constexpr int kDefaultCUs = 256;   // MI355X, when the device cannot be queried
+// blocks per CU the planner aims for (split decode blocks are 8 waves, MLA
+// blocks 4): one wave of resident blocks for the sparse step, several for
+// the long dense stream so that unequal requests even out
+constexpr int kSparseBlocksPerCU = 1;
+constexpr int kFullBlocksPerCU = 16;
 // MLA (4-wave blocks, two resident per CU): the sparse step takes one block
 // per CU.  Its blocks select their pages themselves, so fewer, longer splits
 // repeat less selection and leave the combine fewer partials (MLA step 70.9
 // -> 68.1 us against two per CU); the dense stream keeps two per CU.
-constexpr int kMlaSparseTargetBlocks = kNumCUs;
-constexpr int kMlaFullTargetBlocks = kNumCUs * 2;
+constexpr int kMlaSparseBlocksPerCU = 1;
+constexpr int kMlaFullBlocksPerCU = 2;
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxOrderedBatch = 512;
 constexpr int kMaxCandidates = 16384;
 constexpr int kFusedMaxPages = 6144;
             // page ids + keys in LDS: 48 KiB
 constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
 
-int g_pages_per_split_override = 0;
+// Per-device properties, queried once per device (256 CUs / 64 KiB of LDS
+// per block if a query fails).
+struct DeviceProps {
+  int cus = 0;
+  size_t lds = 0;
+};
 
-// Largest LDS allocation one block may use on the current device (cached
-// per device; 64 KiB if the query fails).
-size_t max_lds_per_block() {
-  static size_t cached[64] = {};
+const DeviceProps& device_props() {
+  static DeviceProps cached[kMaxDevices];
+  static const DeviceProps fallback{kDefaultCUs, 65536};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
-  if (!cached[dev]) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fallback;
+  DeviceProps& p = cached[dev];
+  if (!p.cus) {
     int v = 0;
-    cached[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
-                       hipSuccess && v > 0)
-                      ? (size_t)v
-                      : 65536;
+    p.lds = (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+                 hipSuccess && v > 0)
+                ? (size_t)v
+                : 65536;
+    v = 0;
+    p.cus = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                 hipSuccess && v > 0)
+                ? v
+                : kDefaultCUs;
   }
-  return cached[dev];
+  return p;
 }
+
+// Largest LDS allocation one block may use on the current device.
+size_t max_lds_per_block() { return device_props().lds; }
+// Compute units of the current device.
+int device_cus() { return device_props().cus; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -115,18 +129,23 @@ struct DecodePlan {
   size_t ws_bytes() const { return part_o_bytes + part_ml_bytes; }
 };
 
-// Splits for `pages` pages per (request, KV head).
-DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, bool sparse) {
+// Splits for `pages` pages per (request, KV head) on a GPU of `cus` compute
+// units.  pps_hint > 0 asks for that many pages per split (still at least
+// ceil(pages / kMaxSplits), and at most what the MLA kernel's page list
+// holds).  A pure function of its arguments.
+DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, bool sparse, int cus,
+                       int pps_hint = 0) {
   DecodePlan p;
   const long long units = std::max(1LL, (long long)bt->batch * kv->num_kv_heads);
   const int G = bt->num_q_heads / kv->num_kv_heads;
   pages = std::max(pages, 1);
+  cus = std::max(cus, 1);
   int pps;
-  if (g_pages_per_split_override > 0) {
-    pps = g_pages_per_split_override;
+  if (pps_hint > 0) {
+    pps = pps_hint;
   } else if (is_mla(kv)) {
-    const int n_want =
-        std::max(1, ceil_div(sparse ? kMlaSparseTargetBlocks : kMlaFullTargetBlocks, units));
+    const long long target = (long long)cus * (sparse ? kMlaSparseBlocksPerCU : kMlaFullBlocksPerCU);
+    const int n_want = std::max(1, ceil_div(target, units));
     pps = ceil_div(pages, n_want);
     // partials: G rows of (D_v + 2) fp32, written and read once per split
     // (the reads mostly hit the on-package cache, hence the loose cap)
@@ -135,7 +154,7 @@ DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, boo
            (double)ceil_div(pages, pps) * G * (kv->head_dim_v + 2) * 8 > 0.6 * kv_bytes)
       ++pps;
   } else {
-    const int target = sparse ? kSparseTargetBlocks : kFullTargetBlocks;
+    const long long target = (long long)cus * (sparse ? kSparseBlocksPerCU : kFullBlocksPerCU);
     const int n_want = std::max(1, ceil_div(target, units));
     pps = ceil_div(pages, n_want);
     if (!sparse) pps = std::max(pps, 64);
@@ -157,6 +176,12 @@ DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, boo
   return p;
 }
 
+// Pages per (request, KV head) a decode call walks: the selection's length,
+// or every page the batch can hold.
+int decode_pages(const vx_paged_kv* kv, const vx_batch* bt, bool sparse, int k_tot) {
+  return sparse ? k_tot : max_pages_eff(kv, bt);
+}
+
 size_t score_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt) {
   return align_up((size_t)bt->batch * kv->num_kv_heads * max_pages_eff(kv, bt) * sizeof(float));
 }
@@ -175,9 +200,10 @@ struct SelectInDecode {
 vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
                      const int32_t* sel, int32_t k_tot, float sm_scale, void* out, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream,
-                     const SelectInDecode* fs = nullptr) {
+                     const SelectInDecode* fs = nullptr, const DecodePlan* given = nullptr) {
   const bool sparse = sel != nullptr || fs != nullptr;
-  const DecodePlan p = plan_decode(kv, bt, sparse ? k_tot : max_pages_eff(kv, bt), sparse);
+  const DecodePlan p =
+      given ? *given : plan_decode(kv, bt, decode_pages(kv, bt, sparse, k_tot), sparse, device_cus());
   const size_t off = fs ? fs->ws_offset : 0;
   if (ws_bytes < off + p.ws_bytes()) return VX_ERR_WORKSPACE_TOO_SMALL;
   if (p.ws_bytes() > 0 && ws == nullptr) return VX_ERR_INVALID_ARGUMENT;
@@ -290,7 +316,7 @@ vx_status score_topk_impl(const vx_paged_kv* kv, const vx_batch* batch, const vo
   // the GPU (or the whole problem is tiny) and the candidate keys fit in LDS.
   const long long units = (long long)batch->batch * kv->num_kv_heads;
   if (fused_indexer_supported(kv->dtype, kv->head_dim_qk) && mp <= kFusedMaxPages &&
-      (units >= kNumCUs / 2 || units * mp <= 4096)) {
+      (units >= device_cus() / 2 || units * mp <= 4096)) {
     ScoreArgs s{};
     s.q = q;
     s.cent = kv->centroids;
@@ -365,7 +391,7 @@ hipError_t launch_completed_bounds(const vx_paged_kv* kv, const vx_batch* batch,
 // per CU in all, each request's candidates cut into ceil(256 / B) chunks (a
 // multiple of 8 pages, at least 32).
 int split_score_chunk(const vx_batch* batch, int max_cand) {
-  const int nblk = std::max(1, ceil_div(kNumCUs, batch->batch));
+  const int nblk = std::max(1, ceil_div(device_cus(), batch->batch));
   const int cpb = ceil_div(max_cand, nblk);
   return std::max(32, (cpb + 7) / 8 * 8);
 }
@@ -440,7 +466,7 @@ hipError_t launch_split_bound_score(const vx_paged_kv* kv, const vx_batch* batch
 size_t step_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
   // the indexer's scores and the decode partials side by side (the decode
   // kernel may select from the scores while it writes partials)
-  return align_up(score_ws_bytes(kv, bt)) + plan_decode(kv, bt, k_tot, true).ws_bytes();
+  return align_up(score_ws_bytes(kv, bt)) + plan_decode(kv, bt, k_tot, true, device_cus()).ws_bytes();
 }
 
 // Dynamic LDS of the fused step kernel: staged page row and keys (one word
@@ -473,7 +499,7 @@ vx_status full_decode_check(const vx_paged_kv* kv, const vx_batch* batch, const 
   if (!q || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) || !batch->page_table ||
       !batch->seq_lens)
     return VX_ERR_INVALID_ARGUMENT;
-  const DecodePlan p = plan_decode(kv, batch, max_pages_eff(kv, batch), false);
+  const DecodePlan p = plan_decode(kv, batch, max_pages_eff(kv, batch), false, device_cus());
   if (workspace_bytes < p.ws_bytes()) return VX_ERR_WORKSPACE_TOO_SMALL;
   if (p.ws_bytes() > 0 && !workspace) return VX_ERR_INVALID_ARGUMENT;
   return VX_OK;
@@ -505,7 +531,7 @@ vx_status step_check(const vx_paged_kv* kv, const vx_batch* batch, const void* s
 // Workspace of vx_decode_layers: the larger of a step's and a dense call's.
 size_t layers_ws_bytes(const vx_paged_kv* kv, const vx_batch* bt, int k_tot) {
   return std::max(step_ws_bytes(kv, bt, k_tot),
-                  plan_decode(kv, bt, max_pages_eff(kv, bt), false).ws_bytes());
+                  plan_decode(kv, bt, max_pages_eff(kv, bt), false, device_cus()).ws_bytes());
 }
 
 bool same_shape(const vx_paged_kv& a, const vx_paged_kv& b) {
@@ -635,7 +661,7 @@ vx_status vx_score_topk_bounds(const vx_paged_kv* kv, const vx_batch* batch, con
   // selecting when such blocks fill the GPU, else the split scorer + K3
   const long long units = (long long)batch->batch * kv->num_kv_heads;
   if (fused_indexer_supported(kv->dtype, kv->head_dim_qk) && mp <= kFusedMaxPages &&
-      (units >= kNumCUs / 2 || units * mp <= 4096)) {
+      (units >= device_cus() / 2 || units * mp <= 4096)) {
     ScoreArgs s{};
     s.q = q;
     s.cent = bounds;
@@ -734,10 +760,11 @@ vx_status decode_step_impl(const vx_paged_kv* kv, const vx_batch* batch, bool us
   // With two or more units per CU: 4-wave blocks, two resident per CU, and
   // (up to 512 requests, where ranking them costs each block little) rows of
   // blocks taken longest request first.
-  const int waves = units >= 2 * kNumCUs ? 4 : 8;
+  const int cus = device_cus();
+  const int waves = units >= 2 * cus ? 4 : 8;
   const int ordered = (waves == 4 && batch->batch <= kMaxOrderedBatch) ? batch->batch : 0;
   if (!is_mla(kv) && decode_step_supported(kv->dtype, kv->head_dim_qk, G) &&
-      (units >= kNumCUs / 2 || units * mp <= 4096) &&
+      (units >= cus / 2 || units * mp <= 4096) &&
       step_lds_bytes(mp, k_tot, kv->head_dim_qk, G, ordered, use_bounds) <= max_lds_per_block()) {
     StepArgs a{};
     DecodeArgs& d = a.d;
@@ -797,7 +824,7 @@ vx_status decode_step_impl(const vx_paged_kv* kv, const vx_batch* batch, bool us
   const int max_cand = std::max(mp - n_bos - n_eos, 0);
   const bool split_scorer = !(fused_indexer_supported(kv->dtype, kv->head_dim_qk) &&
                               mp <= kFusedMaxPages &&
-                              (units >= kNumCUs / 2 || units * mp <= 4096));
+                              (units >= cus / 2 || units * mp <= 4096));
   const size_t sel_lds = (size_t)(round4(mp) + k_tot) * 4 + kSelectLdsBytes +
                          attention_lds_bytes(kv->head_dim_qk, G);
   const bool select_fits = is_mla(kv) ? mla_select_fits(mp, k_tot)
@@ -908,10 +935,10 @@ vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* b
       return VX_OK;
     case VX_OP_SPARSE_DECODE:
       if (k_tot < 1) return VX_ERR_INVALID_ARGUMENT;
-      *bytes = plan_decode(kv, batch, k_tot, true).ws_bytes();
+      *bytes = plan_decode(kv, batch, k_tot, true, device_cus()).ws_bytes();
       return VX_OK;
     case VX_OP_FULL_DECODE:
-      *bytes = plan_decode(kv, batch, max_pages_eff(kv, batch), false).ws_bytes();
+      *bytes = plan_decode(kv, batch, max_pages_eff(kv, batch), false, device_cus()).ws_bytes();
       return VX_OK;
     case VX_OP_DECODE_STEP:
       if (max_pages_eff(kv, batch) > kMaxCandidates) return VX_ERR_UNSUPPORTED;
@@ -927,10 +954,59 @@ vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* b
   return VX_ERR_INVALID_ARGUMENT;
 }
 
-vx_status vx_set_pages_per_split(int32_t pages_per_split) {
-  if (pages_per_split < 0) return VX_ERR_INVALID_ARGUMENT;
-  g_pages_per_split_override = pages_per_split;
+vx_status vx_plan_decode(int32_t op, const vx_paged_kv* kv, const vx_batch* batch, int32_t k_tot,
+                         int32_t num_cus, int32_t pages_per_split, vx_decode_plan* plan) {
+  if (!plan) return VX_ERR_INVALID_ARGUMENT;
+  vx_status st = check_kv(kv);
+  if (st != VX_OK) return st;
+  if ((st = check_batch(kv, batch)) != VX_OK) return st;
+  if (op != VX_OP_SPARSE_DECODE && op != VX_OP_FULL_DECODE) return VX_ERR_INVALID_ARGUMENT;
+  if (num_cus < 0 || pages_per_split < 0) return VX_ERR_INVALID_ARGUMENT;
+  const bool sparse = op == VX_OP_SPARSE_DECODE;
+  if (sparse && k_tot < 1) return VX_ERR_INVALID_ARGUMENT;
+  const int cus = num_cus > 0 ? num_cus : device_cus();
+  const DecodePlan p = plan_decode(kv, batch, decode_pages(kv, batch, sparse, k_tot), sparse, cus,
+                                   pages_per_split);
+  *plan = vx_decode_plan{};
+  plan->op = op;
+  plan->num_cus = cus;
+  plan->pages_per_split = p.pages_per_split;
+  plan->n_split = p.n_split;
+  plan->workspace_bytes = p.ws_bytes();
   return VX_OK;
+}
+
+vx_status vx_paged_decode_planned(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                                  const int32_t* sel, int32_t k_tot, const vx_decode_plan* plan,
+                                  float sm_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (!plan) return VX_ERR_INVALID_ARGUMENT;
+  const bool sparse = plan->op == VX_OP_SPARSE_DECODE;
+  vx_decode_plan again{};
+  if (plan->num_cus < 1) return VX_ERR_INVALID_ARGUMENT;
+  const vx_status st = vx_plan_decode(plan->op, kv, batch, k_tot, plan->num_cus,
+                                      plan->pages_per_split, &again);
+  if (st != VX_OK) return st;
+  // the plan must be one vx_plan_decode made for these shapes
+  if (again.num_cus != plan->num_cus || again.pages_per_split != plan->pages_per_split ||
+      again.n_split != plan->n_split || again.workspace_bytes != plan->workspace_bytes ||
+      plan->reserved_[0] != 0 || plan->reserved_[1] != 0 || (sparse != (sel != nullptr)))
+    return VX_ERR_INVALID_ARGUMENT;
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
+  if (batch->batch == 0) return VX_OK;
+  if (!q || !out || !kv->k_cache || (!kv->v_aliases_k && !kv->v_cache) || !batch->page_table ||
+      !batch->seq_lens)
+    return VX_ERR_INVALID_ARGUMENT;
+  DecodePlan p;
+  p.pages_per_split = plan->pages_per_split;
+  p.n_split = plan->n_split;
+  if (p.n_split > 1) {
+    const size_t rows = (size_t)batch->batch * batch->num_q_heads * p.n_split;
+    p.part_o_bytes = align_up(rows * kv->head_dim_v * sizeof(float));
+    p.part_ml_bytes = align_up(rows * 2 * sizeof(float));
+  }
+  return run_decode(kv, batch, q, sel, sparse ? k_tot : 0, sm_scale, out, lse, workspace,
+                    workspace_bytes, stream, nullptr, &p);
 }
 
 const char* vx_status_string(vx_status status) {

@@ -131,14 +131,32 @@ __device__ __forceinline__ void attend_pages_valu(const DecodeArgs& a, int b, in
           l[g] += p;
         }
       }
+      if (tok0 + kChunk <= seq) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        float vf[E];
-        V::unpack(vd[i], vf);
+        for (int i = 0; i < NL; ++i) {
+          float vf[E];
+          V::unpack(vd[i], vf);
 #pragma unroll
-        for (int g = 0; g < HG; ++g)
+          for (int g = 0; g < HG; ++g)
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[g][e] = fmaf(s[g][i], vf[e], o[g][e]);
+            for (int e = 0; e < E; ++e) o[g][e] = fmaf(s[g][i], vf[e], o[g][e]);
+        }
+      } else {
+        // The chunk reaches past seq (the unwritten tail of the last page;
+        // the same in every lane): those rows have weight 0, but 0 * NaN or
+        // 0 * Inf would still reach the sum, so their values count as 0.
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const bool valid = tok0 + i * R + grp < seq;
+          float vf[E];
+          V::unpack(vd[i], vf);
+#pragma unroll
+          for (int e = 0; e < E; ++e) vf[e] = valid ? vf[e] : 0.f;
+#pragma unroll
+          for (int g = 0; g < HG; ++g)
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[g][e] = fmaf(s[g][i], vf[e], o[g][e]);
+        }
       }
     };
 #pragma unroll
@@ -308,6 +326,17 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
       for (int r = 0; r < VL; ++r) {
         const int seg = r * 64 + lane, row = seg / (D / 8), col = seg % (D / 8);
         st16(vbuf + row * VROW + 16 * col, vd[r]);
+      }
+      if (tok0 + kChunk > seq) {
+        // Rows at or past seq (the unwritten tail of the last page) have
+        // weight 0, but 0 * NaN would still reach O: each lane overwrites
+        // its own segments of them with zeros (program order makes the
+        // zeros win).
+#pragma unroll
+        for (int r = 0; r < VL; ++r) {
+          const int seg = r * 64 + lane, row = seg / (D / 8), col = seg % (D / 8);
+          if (tok0 + row >= seq) st16(vbuf + row * VROW + 16 * col, make_uint4(0u, 0u, 0u, 0u));
+        }
       }
       // S^T = K Q^T
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};

@@ -193,11 +193,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
       const int row = c / kChunksPerRow, col = c - row * kChunksPerRow;
       st16(ktile + row * kLdsRow + col * 16, regs[r]);
     }
+    const int j = t / (kPage / kT), half = t % (kPage / kT);
+    const int tok0 = page_logi[j] * kPage + half * kT;
+    if (tok0 + kT > seq) {
+      // Rows at or past seq (the unwritten tail of the last page): their
+      // scores are masked, but as V rows 0 * NaN would still reach O, so
+      // each thread overwrites its own chunks of them with zeros (program
+      // order within the thread makes the zeros win).
+#pragma unroll
+      for (int r = 0; r < kLoads; ++r) {
+        const int c = tid + r * kThreads;
+        const int row = c / kChunksPerRow, col = c - row * kChunksPerRow;
+        if (tok0 + row >= seq) st16(ktile + row * kLdsRow + col * 16, make_uint4(0u, 0u, 0u, 0u));
+      }
+    }
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(t + 1);
 
-    const int j = t / (kPage / kT), half = t % (kPage / kT);
-    const int tok0 = page_logi[j] * kPage + half * kT;
 
     // ---- partial S^T over dims 144w .. 144w + 143
     f32x16 sp;

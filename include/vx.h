@@ -28,8 +28,8 @@
  *               only and are not retained.
  *   Ownership.  The caller owns every buffer.  The library never
  *               allocates or frees device memory and keeps no state across
- *               calls except cached device properties and the split
- *               override below; calls are reentrant.
+ *               calls except cached device properties (compute-unit count,
+ *               LDS per block); calls are reentrant.
  *   Streams.    Work is enqueued on `stream` (NULL = the null stream);
  *               calls return after launch, never synchronise the host.
  *   Errors.     Arguments are validated on the host before any HIP call;
@@ -347,15 +347,47 @@ vx_status vx_decode_layers(const vx_paged_kv* kv, const vx_batch* batch, const v
 
 /* Workspace bytes the call `op` needs for these shapes (k_tot is read for
  * VX_OP_SPARSE_DECODE, VX_OP_DECODE_STEP and VX_OP_DECODE_LAYERS only).
- * Host-only; never touches the GPU.  The size depends on the shapes and on
- * the split override, nothing else. */
+ * Host-only; launches nothing.  The size depends on the shapes and on the
+ * current device's compute-unit count (256 when it cannot be queried). */
 vx_status vx_workspace_size(int32_t op, const vx_paged_kv* kv, const vx_batch* batch,
                             int32_t k_tot, size_t* bytes /* host */);
 
-/* Test hook: force every decode split to cover `pages_per_split` pages
- * (0 restores the planner).  Process-wide; not for concurrent use with
- * other calls.  Returns VX_ERR_INVALID_ARGUMENT for a negative value. */
-vx_status vx_set_pages_per_split(int32_t pages_per_split);
+/* A decode launch plan (the article's "workload planner for balanced GPU
+ * scheduling", section "A dual-stage programmable abstraction"): how
+ * vx_sparse_paged_decode / vx_full_paged_decode cut each (request, KV head)'s
+ * page list into splits of consecutive entries, merged afterwards.  Those
+ * calls plan for the current device themselves; an explicit plan is for
+ * callers that want a launch independent of the device (the same plan on GPUs
+ * of different sizes, or a fixed split size).  The output does not depend on
+ * the plan beyond the order of fp32 rounding. */
+typedef struct {
+  int32_t op;               /* VX_OP_SPARSE_DECODE or VX_OP_FULL_DECODE          */
+  int32_t num_cus;          /* compute units the plan was made for               */
+  int32_t pages_per_split;  /* list entries one split attends                    */
+  int32_t n_split;          /* splits per (request, KV head); 1: direct output   */
+  int32_t reserved_[2];     /* 0                                                 */
+  uint64_t workspace_bytes; /* workspace the planned call needs                  */
+} vx_decode_plan;
+
+/* Plans the decode call `op` for these shapes (k_tot read for
+ * VX_OP_SPARSE_DECODE only) on a GPU of `num_cus` compute units (0: the
+ * current device's), with `pages_per_split` pages per split (0: the
+ * planner's choice; a given value is raised to ceil(pages / 1024) and, for
+ * MLA shapes, capped at 256).  Host-only and a pure function of its
+ * arguments (and, for num_cus 0, of the device's CU count); writes *plan. */
+vx_status vx_plan_decode(int32_t op, const vx_paged_kv* kv, const vx_batch* batch, int32_t k_tot,
+                         int32_t num_cus, int32_t pages_per_split, vx_decode_plan* plan /* host */);
+
+/* vx_sparse_paged_decode (sel given, plan->op VX_OP_SPARSE_DECODE) or
+ * vx_full_paged_decode (sel NULL, plan->op VX_OP_FULL_DECODE) launched with
+ * an explicit plan.  The plan must be what vx_plan_decode returns for these
+ * shapes, its num_cus and its pages_per_split (VX_ERR_INVALID_ARGUMENT
+ * otherwise); the workspace must hold plan->workspace_bytes.  Other
+ * arguments and errors as for those calls. */
+vx_status vx_paged_decode_planned(const vx_paged_kv* kv, const vx_batch* batch, const void* q,
+                                  const int32_t* sel, int32_t k_tot, const vx_decode_plan* plan,
+                                  float sm_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* vx_status_string(vx_status status);

@@ -49,6 +49,7 @@ class Case:
     q_host: torch.Tensor | None = None          # [B, H_q, D] in the workload dtype
     attempts: np.ndarray | None = None
     _oracle_cent: dict = field(default_factory=dict)
+    _oracle_bounds: dict = field(default_factory=dict)
 
     @property
     def L(self) -> np.ndarray:
@@ -79,6 +80,15 @@ class Case:
             self._oracle_cent[key] = orc.request_centroids(k_pages, int(self.L[b]), self.w.dtype)
         return self._oracle_cent[key]
 
+    def oracle_bounds(self, b: int) -> np.ndarray:
+        """Oracle key bounds [n_b, H_kv, 2, D] of request b at the current step."""
+        key = (b, int(self.L[b]) // self.w.page_size)
+        if key not in self._oracle_bounds:
+            k_pages, _ = self.request_pages(b)
+            n_b = self.n_pages(b)
+            self._oracle_bounds[key] = orc.request_bounds(k_pages, int(self.L[b]))[:n_b]
+        return self._oracle_bounds[key]
+
 
 def setup_case(vx, w: synth.Workload, device="cuda") -> Case:
     lay = synth.build_layout(w)
@@ -101,6 +111,58 @@ def set_step(c: Case, step: int):
     c.q_host = synth.make_queries(c.w, c.layout, step)
 
 
+def page_sums_fp64(c: Case, b: int) -> np.ndarray:
+    """Sum over each full page's tokens of request b's keys, in fp64 on the
+    device: [n_full, H_kv, D].  For bf16 keys the sum of 16 or 64 values is
+    exact in fp64 (each has an 8-bit significand; the exponents of the values
+    drawn here span far fewer than the 41 binades that would take), so it
+    equals the sum numpy forms for the oracle's mean, whatever the order."""
+    n_full = int(c.L[b]) // c.w.page_size
+    idx = c.pt[b, :n_full].long()
+    return c.K[idx].double().sum(dim=2).cpu().numpy()
+
+
+def prime_centroids_device(c: Case, requests):
+    """Fill the oracle-centroid cache of the listed requests from exact fp64
+    page sums formed on the device (bf16 only, see page_sums_fp64), divided
+    by the page size and rounded by the oracle's own round_to.  Equal bit for
+    bit to orc.request_centroids (pinned by test_device_centroid_shortcut);
+    used where the oracle's host pass over every page of a full-size batch
+    would take minutes."""
+    w = c.w
+    assert w.dtype == "bf16", "exact fp64 page sums need bf16 keys"
+    for b in requests:
+        key = (b, int(c.L[b]) // w.page_size)
+        if key in c._oracle_cent:
+            continue
+        n_b = c.n_pages(b)
+        out = np.full((n_b, w.num_kv_heads, w.head_dim_qk), np.nan)
+        n_full = int(c.L[b]) // w.page_size
+        if n_full:
+            out[:n_full] = orc.round_to(page_sums_fp64(c, b) / w.page_size, w.dtype)
+        c._oracle_cent[key] = out
+
+
+def prime_bounds_device(c: Case, requests):
+    """Fill the oracle-bounds cache of the listed requests with per-channel
+    minima and maxima taken on the device.  Minimum and maximum are exact in
+    any order, so these equal orc.request_bounds (pinned by
+    test_device_bounds_shortcut)."""
+    w = c.w
+    for b in requests:
+        key = (b, int(c.L[b]) // w.page_size)
+        if key in c._oracle_bounds:
+            continue
+        n_b = c.n_pages(b)
+        out = np.full((n_b, w.num_kv_heads, 2, w.head_dim_qk), np.nan)
+        n_full = int(c.L[b]) // w.page_size
+        if n_full:
+            kk = c.K[c.pt[b, :n_full].long()]
+            out[:n_full, :, 0] = kk.amin(dim=2).double().cpu().numpy()
+            out[:n_full, :, 1] = kk.amax(dim=2).double().cpu().numpy()
+        c._oracle_bounds[key] = out
+
+
 def gap_ok(scores: np.ndarray, k: int) -> bool:
     if len(scores) <= k or k == 0:
         return True
@@ -108,9 +170,11 @@ def gap_ok(scores: np.ndarray, k: int) -> bool:
     return (s[k - 1] - s[k]) > GAP_REL * np.max(np.abs(scores))
 
 
-def fix_gaps(c: Case, requests) -> int:
+def fix_gaps(c: Case, requests, rule: str = "centroid") -> int:
     """Redraw query groups of the listed requests until every group's score
-    gap is wide enough.  Returns the number of redraws."""
+    gap is wide enough.  ``rule`` "centroid" scores by the oracle centroids,
+    "bounds" by Quest's criticality over the oracle key bounds.  Returns the
+    number of redraws."""
     w = c.w
     G = w.group
     redraws = 0
@@ -119,12 +183,15 @@ def fix_gaps(c: Case, requests) -> int:
         cand = orc.candidate_pages(n_b, w.n_bos, w.n_eos)
         if len(cand) <= w.topk:
             continue
-        cent = c.oracle_centroids(b)
+        summ = c.oracle_centroids(b) if rule == "centroid" else c.oracle_bounds(b)
         for h in range(w.num_kv_heads):
             while True:
                 q = c.q_host[b, h * G:(h + 1) * G].to(torch.float64).numpy()
                 qbar = orc.group_mean_query(q, 1)
-                s = orc.page_scores(qbar, cent[:, h:h + 1], cand)[0]
+                if rule == "centroid":
+                    s = orc.page_scores(qbar, summ[:, h:h + 1], cand)[0]
+                else:
+                    s = orc.bound_scores(qbar, summ[:, h:h + 1], cand)[0]
                 if gap_ok(s, w.topk):
                     break
                 c.attempts[b, h] += 1
@@ -134,6 +201,28 @@ def fix_gaps(c: Case, requests) -> int:
                 g = synth.draw_query_group(w, c.layout, c.step, b, h, int(c.attempts[b, h]))
                 c.q_host[b, h * G:(h + 1) * G] = torch.from_numpy(g).to(w.torch_dtype)
     return redraws
+
+
+def oracle_selection(c: Case, b: int, rule: str = "centroid") -> np.ndarray:
+    """The oracle's selection table [H_kv, k_tot] of request b."""
+    w = c.w
+    n_b = c.n_pages(b)
+    q = c.q_host[b].to(torch.float64).numpy()
+    if rule == "centroid":
+        sel = orc.select_pages(q, c.oracle_centroids(b)[:n_b], n_b, w.topk, w.n_bos, w.n_eos)
+    else:
+        sel = orc.select_pages_quest(q, c.oracle_bounds(b), n_b, w.topk, w.n_bos, w.n_eos)
+    return orc.selection_table(sel, w.k_tot)
+
+
+def assert_all_selections(c: Case, sel_dev: torch.Tensor, rule: str = "centroid"):
+    """Every (request, KV head) row of the GPU selection equals the oracle's,
+    bit for bit."""
+    got = sel_dev.cpu().numpy()
+    for b in range(c.w.batch):
+        want = oracle_selection(c, b, rule)
+        bad = np.nonzero((got[b] != want).any(axis=1))[0]
+        assert len(bad) == 0, f"request {b}: selected pages differ on KV heads {bad.tolist()}"
 
 
 def oracle_request(c: Case, b: int, sparse: bool = True):

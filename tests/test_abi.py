@@ -167,7 +167,6 @@ def test_scalar_arguments_rejected(lib):
     assert st == 0 and need >= ws_size(lib, vx.VX_OP_SCORE_TOPK, kv, bt)[1]
     assert step(r(kv), r(bt), FAKE, 30, 1, 1, 1, 0.1, FAKE, FAKE, FAKE, FAKE, need - 1,
                 None) == vx.VX_ERR_WORKSPACE_TOO_SMALL
-    assert lib.vx_set_pages_per_split(-1) == vx.VX_ERR_INVALID_ARGUMENT
     assert lib.vx_workspace_size(9, r(kv), r(bt), 32, r(ctypes.c_size_t())) == 1
 
 
@@ -223,18 +222,73 @@ def test_workspace_monotone_in_shapes(lib):
         assert sizes == sorted(sizes) or op == vx.VX_OP_SPARSE_DECODE
 
 
-def test_split_override_changes_plan(lib):
+def plan(lib, op, kv, bt, k_tot=0, cus=0, pps=0):
+    p = vx.DecodePlanStruct()
+    st = lib.vx_plan_decode(op, ctypes.byref(kv), ctypes.byref(bt), k_tot, cus, pps,
+                            ctypes.byref(p))
+    return st, p
+
+
+@pytest.mark.parametrize("cus", [256, 32])
+def test_plan_is_a_function_of_shapes_and_cus(lib, cus):
+    """The planner on the host, for a full MI355X (256 CUs) and a 32-CU
+    partition: sparse splits aim at one 8-wave block per CU, dense ones at
+    16 per CU (at least 64 pages each), partials within 15% of the K/V bytes
+    they replace, and the workspace holds exactly the partials."""
+    kv = kv_struct()
+    # long context: 8 requests x 8 KV heads, 258 selected pages each
+    bt = batch_struct(batch=8, num_q_heads=64, max_pages_per_req=8192, max_seq_len=131072)
+    st, p = plan(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 258, cus)
+    assert st == 0 and p.num_cus == cus and p.op == vx.VX_OP_SPARSE_DECODE
+    want = -(-258 // -(-cus // 64))                      # ceil(258 / ceil(cus / 64 units))
+    assert p.pages_per_split == want and p.n_split == -(-258 // want)
+    rows = 8 * 64 * p.n_split
+    assert p.workspace_bytes == (0 if p.n_split == 1 else
+                                 -(-rows * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256)
+    # Qwen-like: 256 units, one split per unit on either GPU
+    bt2 = batch_struct(batch=32, num_q_heads=16, max_pages_per_req=2048, max_seq_len=32768)
+    st, p = plan(lib, vx.VX_OP_SPARSE_DECODE, kv, bt2, 32, cus)
+    assert st == 0 and p.n_split == 1 and p.workspace_bytes == 0
+    # dense: 2048 pages over ceil(16 cus / 256) splits, at least 64 pages each
+    st, p = plan(lib, vx.VX_OP_FULL_DECODE, kv, bt2, 0, cus)
+    n_want = -(-16 * cus // 256)
+    assert st == 0 and p.pages_per_split == max(-(-2048 // n_want), 64)
+    # the same shapes always give the same plan
+    assert plan(lib, vx.VX_OP_FULL_DECODE, kv, bt2, 0, cus)[1].pages_per_split == p.pages_per_split
+
+
+def test_plan_with_a_fixed_split_size(lib):
     kv = kv_struct()
     bt = batch_struct(batch=2, max_pages_per_req=256, max_seq_len=4096)
-    try:
-        assert lib.vx_set_pages_per_split(1) == 0
-        _, n1 = ws_size(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32)
-        assert n1 >= 2 * 16 * 32 * 128 * 4                  # 32 splits of fp32 partials
-        assert lib.vx_set_pages_per_split(1000) == 0
-        _, n2 = ws_size(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32)
-        assert n2 == 0                                      # one split: direct output
-    finally:
-        lib.vx_set_pages_per_split(0)
+    st, p1 = plan(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32, 256, 1)
+    assert st == 0 and p1.pages_per_split == 1 and p1.n_split == 32
+    assert p1.workspace_bytes >= 2 * 16 * 32 * 128 * 4                 # 32 splits of fp32 partials
+    st, p2 = plan(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32, 256, 1000)
+    assert st == 0 and p2.n_split == 1 and p2.workspace_bytes == 0     # one split: direct output
+    st, p3 = plan(lib, vx.VX_OP_FULL_DECODE, kv, bt, 0, 256, 0)
+    assert st == 0 and p3.pages_per_split >= 64
+    r = ctypes.byref
+    for bad in ((vx.VX_OP_SCORE_TOPK, 32, 256, 0), (vx.VX_OP_SPARSE_DECODE, 0, 256, 0),
+                (vx.VX_OP_SPARSE_DECODE, 32, -1, 0), (vx.VX_OP_SPARSE_DECODE, 32, 256, -2)):
+        assert plan(lib, bad[0], kv, bt, bad[1], bad[2], bad[3])[0] == vx.VX_ERR_INVALID_ARGUMENT
+    assert lib.vx_plan_decode(vx.VX_OP_FULL_DECODE, r(kv), r(bt), 0, 256, 0,
+                              None) == vx.VX_ERR_INVALID_ARGUMENT
+    # a planned call checks its plan against the planner before launching anything
+    run = lib.vx_paged_decode_planned
+    forged = vx.DecodePlanStruct.from_buffer_copy(p1)
+    forged.n_split = 7
+    assert run(r(kv), r(bt), FAKE, FAKE, 32, r(forged), 0.1, FAKE, FAKE, FAKE, 1 << 30,
+               None) == vx.VX_ERR_INVALID_ARGUMENT
+    assert run(r(kv), r(bt), FAKE, None, 32, r(p1), 0.1, FAKE, FAKE, FAKE, 1 << 30,
+               None) == vx.VX_ERR_INVALID_ARGUMENT                     # sparse plan, no sel
+    assert run(r(kv), r(bt), FAKE, FAKE, 32, r(p1), 0.1, FAKE, FAKE, FAKE, p1.workspace_bytes - 1,
+               None) == vx.VX_ERR_WORKSPACE_TOO_SMALL
+    empty = batch_struct(batch=0)
+    st, p0 = plan(lib, vx.VX_OP_SPARSE_DECODE, kv, empty, 32, 256, 1)
+    assert st == 0 and p0.workspace_bytes == 0
+    assert run(r(kv), r(empty), None, FAKE, 32, r(p0), 0.1, None, None, None, 0, None) == vx.VX_OK
+    assert run(r(kv), r(empty), None, FAKE, 32, r(p1), 0.1, None, None, None, 0,
+               None) == vx.VX_ERR_INVALID_ARGUMENT                     # planned for 2 requests
 
 
 def test_radix_and_append_arguments_rejected(lib):

@@ -24,7 +24,6 @@ def vx():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import block_sparse_paged_amd as m
     m.load_library()
-    m.set_pages_per_split(0)
     return m
 
 
