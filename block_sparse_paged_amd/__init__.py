@@ -37,7 +37,12 @@ EXPORTS = ("vx_centroid_update", "vx_append_kv", "vx_score_topk", "vx_score_topk
            "vx_sparse_paged_decode",
            "vx_full_paged_decode", "vx_sparse_decode_step", "vx_sparse_decode_step_bounds",
            "vx_decode_layers", "vx_plan_decode", "vx_paged_decode_planned",
+           "vx_sparse_decode_step_static",
            "vx_workspace_size", "vx_status_string", "vx_version")
+
+# Bytes of the static device scratch behind vx_sparse_decode_step_static
+# (VX_STATIC_SCRATCH_BYTES in include/vx.h).
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class VxError(RuntimeError):
@@ -98,6 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vx_full_paged_decode.argtypes = [kvp, btp, VP, F32, VP, VP, VP, SZ, VP]
     lib.vx_sparse_decode_step.argtypes = [kvp, btp, VP, I32, I32, I32, I32, F32, VP, VP, VP,
                                           VP, SZ, VP]
+    lib.vx_sparse_decode_step_static.argtypes = [kvp, btp, VP, I32, I32, I32, I32, F32, VP, VP,
+                                                 VP, VP]
     lib.vx_sparse_decode_step_bounds.argtypes = [kvp, btp, VP, VP, I32, I32, I32, I32, F32, VP,
                                                  VP, VP, VP, SZ, VP]
     lib.vx_decode_layers.argtypes = [kvp, btp, VP, I32, VP, I32, I32, I32, I32, F32, VP, VP, VP,
@@ -114,7 +121,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                  "vx_sparse_paged_decode",
                  "vx_full_paged_decode", "vx_sparse_decode_step", "vx_sparse_decode_step_bounds",
                  "vx_decode_layers", "vx_plan_decode", "vx_paged_decode_planned",
-                 "vx_workspace_size", "vx_version"):
+                 "vx_sparse_decode_step_static", "vx_workspace_size", "vx_version"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -332,6 +339,23 @@ def sparse_decode_step(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_
     """vx_sparse_decode_step: completed-page centroids, selection and attention."""
     prepare_sparse_decode_step(kv, batch, q, topk, n_bos, n_eos, update_completed, sm_scale,
                                sel, out, lse, workspace, stream)()
+
+
+def sparse_decode_step_static(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
+                              n_eos: int, update_completed: bool, sm_scale: float,
+                              sel: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor],
+                              stream=None):
+    """vx_sparse_decode_step_static: the decode step with the library's static
+    device scratch as its workspace (no allocation; calls that overlap on one
+    GPU race)."""
+    _need(q, "q")
+    _need(sel, "sel", torch.int32)
+    _need(out, "out")
+    kvs, bs = kv.struct(), batch.struct()
+    _check(load_library().vx_sparse_decode_step_static(
+        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos,
+        1 if update_completed else 0, float(sm_scale), _ptr(sel), _ptr(out), _ptr(lse),
+        _stream(stream)), "vx_sparse_decode_step_static")
 
 
 def sparse_decode_step_bounds(kv: PagedKV, batch: Batch, bounds: torch.Tensor, q: torch.Tensor,

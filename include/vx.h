@@ -314,6 +314,26 @@ vx_status vx_sparse_decode_step_bounds(const vx_paged_kv* kv, const vx_batch* ba
                                        int32_t* sel, void* out, float* lse, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * vx_sparse_decode_step with its workspace taken from a library-owned static
+ * device array of VX_STATIC_SCRATCH_BYTES (one per GPU, held until the
+ * process ends) instead of an argument.  Same results as
+ * vx_sparse_decode_step with a workspace of its own.
+ *   - Allocates nothing (no hipMalloc / hipFree); the first call on a device
+ *     looks the array's address up on that device.
+ *   - Shapes whose VX_OP_DECODE_STEP workspace exceeds VX_STATIC_SCRATCH_BYTES
+ *     return VX_ERR_WORKSPACE_TOO_SMALL with nothing launched.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (concurrent streams, or host threads) race and must be serialised
+ *     by the caller.  The array's contents on entry do not matter.
+ * Other arguments and errors as for vx_sparse_decode_step. */
+#define VX_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+vx_status vx_sparse_decode_step_static(const vx_paged_kv* kv, const vx_batch* batch,
+                                       const void* q, int32_t topk, int32_t n_bos, int32_t n_eos,
+                                       int32_t update_completed, float sm_scale, int32_t* sel,
+                                       void* out, float* lse, hipStream_t stream);
+
 /* The attention layers of one decode step in one call (README, "Using
  * Your Sparse Attention with SGLang": with sparsity on, the layers listed as
  * skipped run full attention; the serving setting replays the step as a

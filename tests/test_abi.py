@@ -424,3 +424,24 @@ def test_step_bounds_arguments_rejected(lib):
     assert call(kv=kv_struct(centroids=None), bounds=None) == vx.VX_ERR_INVALID_ARGUMENT
     assert call(bt=batch_struct(batch=0), bounds=None, q=None, sel=None, out=None,
                 ws=None) == vx.VX_OK
+
+
+def test_static_step_refuses_shapes_beyond_its_scratch(lib):
+    """vx_sparse_decode_step_static checks the shapes' workspace against its
+    static scratch (VX_STATIC_SCRATCH_BYTES) on the host, before any HIP
+    call: too large is VX_ERR_WORKSPACE_TOO_SMALL, an empty batch is a
+    no-op, invalid arguments are rejected as vx_sparse_decode_step rejects
+    them."""
+    r = ctypes.byref
+    kv = kv_struct()
+    big = batch_struct(batch=4096, max_pages_per_req=16384, max_seq_len=16384 * 16)
+    st, need = ws_size(lib, vx.VX_OP_DECODE_STEP, kv, big, 32)
+    assert st == 0 and need > vx.STATIC_SCRATCH_BYTES
+    step = lib.vx_sparse_decode_step_static
+    assert step(r(kv), r(big), FAKE, 30, 1, 1, 1, 0.1, FAKE, FAKE, FAKE,
+                None) == vx.VX_ERR_WORKSPACE_TOO_SMALL
+    assert step(r(kv), r(batch_struct(batch=0)), None, 30, 1, 1, 1, 0.1, None, None, None,
+                None) == vx.VX_OK
+    for topk, bos, eos in ((-1, 1, 1), (30, -1, 1), (30, 1, 0)):
+        assert step(r(kv), r(batch_struct()), FAKE, topk, bos, eos, 1, 0.1, FAKE, FAKE, FAKE,
+                    None) == vx.VX_ERR_INVALID_ARGUMENT
