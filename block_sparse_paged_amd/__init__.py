@@ -159,14 +159,29 @@ class PagedKV:
 
     def struct(self) -> PagedKVStruct:
         k = self.k_cache
+        if k.dim() != 4:
+            raise ValueError(f"k_cache must be [P, H_kv, S_p, D], got shape {tuple(k.shape)}")
+        if k.dtype not in _DT:
+            raise ValueError(f"k_cache must be float32 or bfloat16, got {k.dtype}")
+        _need(k, "k_cache")
         P, H, S, D = k.shape
+        if self.v_cache is not None:
+            v = self.v_cache
+            _need(v, "v_cache", k.dtype)
+            if v.dim() != 4 or tuple(v.shape[:3]) != (P, H, S):
+                raise ValueError(f"v_cache must be [{P}, {H}, {S}, D_v], got {tuple(v.shape)}")
+        if self.centroids is not None:
+            _need(self.centroids, "centroids", k.dtype)
+            if tuple(self.centroids.shape) != (P, H, D):
+                raise ValueError(f"centroids must be [{P}, {H}, {D}], got "
+                                 f"{tuple(self.centroids.shape)}")
         dv = self.v_cache.shape[-1] if self.v_cache is not None else (self.head_dim_v or D)
         return PagedKVStruct(
-            dtype=_DT.get(k.dtype, -1), num_pages=P, page_size=S, num_kv_heads=H,
+            dtype=_DT[k.dtype], num_pages=P, page_size=S, num_kv_heads=H,
             head_dim_qk=D, head_dim_v=dv, v_aliases_k=1 if self.v_cache is None else 0,
             reserved_=0, k_cache=k.data_ptr(),
             v_cache=None if self.v_cache is None else self.v_cache.data_ptr(),
-            centroids=self.centroids.data_ptr())
+            centroids=None if self.centroids is None else self.centroids.data_ptr())
 
 
 @dataclass
@@ -178,18 +193,46 @@ class Batch:
     max_seq_len: int                       # host-side bound used for planning
 
     def struct(self) -> BatchStruct:
+        if self.page_table.dim() != 2:
+            raise ValueError("page_table must be [B, max_pages]")
+        _need(self.page_table, "page_table", torch.int32)
+        _need(self.seq_lens, "seq_lens", torch.int32)
         B, mp = self.page_table.shape
+        if tuple(self.seq_lens.shape) != (B,):
+            raise ValueError(f"seq_lens must be [{B}], got {tuple(self.seq_lens.shape)}")
         return BatchStruct(batch=B, num_q_heads=self.num_q_heads, max_pages_per_req=mp,
                            max_seq_len=int(self.max_seq_len),
                            page_table=self.page_table.data_ptr(),
                            seq_lens=self.seq_lens.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype=None):
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _args(kv: "PagedKV", batch: "Batch", q=None, out=None, sel=None, lse=None):
+    """Checks the tensors of a call against the cache and batch shapes: q
+    [B, H_q, D_qk] and out [B, H_q, D_v] in the cache dtype, sel int32
+    [B, H_kv, k_tot], lse float32 [B, H_q]; every tensor contiguous."""
+    k = kv.k_cache
+    B = batch.page_table.shape[0]
+    H_q, H_kv, D = batch.num_q_heads, k.shape[1], k.shape[3]
+    Dv = kv.v_cache.shape[-1] if kv.v_cache is not None else (kv.head_dim_v or D)
+    if q is not None:
+        _need(q, "q", k.dtype, (B, H_q, D))
+    if out is not None:
+        _need(out, "out", k.dtype, (B, H_q, Dv))
+    if sel is not None:
+        _need(sel, "sel", torch.int32)
+        if sel.dim() != 3 or tuple(sel.shape[:2]) != (B, H_kv):
+            raise ValueError(f"sel must be [{B}, {H_kv}, k_tot], got {tuple(sel.shape)}")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H_q))
 
 
 def workspace_size(op: int, kv: PagedKV, batch: Batch, k_tot: int = 0) -> int:
@@ -247,8 +290,7 @@ def prepare_append_kv(kv: PagedKV, batch: Batch, k_src, v_src, src_start, n_new,
 def score_topk(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
                n_eos: int, sel: torch.Tensor, workspace: torch.Tensor, stream=None):
     """vx_score_topk: selected logical pages per (request, KV head) into sel."""
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
+    _args(kv, batch, q=q, sel=sel)
     kvs, bs = kv.struct(), batch.struct()
     _check(load_library().vx_score_topk(
         ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, _ptr(sel),
@@ -262,8 +304,7 @@ def score_topk_radix(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bo
     levels, then the boundary bin's members by rank from ``rnd``) into sel.
     ``rnd`` holds one random 32-bit word per (request, KV head) (int32 or
     uint32 tensor of B * H_kv elements, read as uint32)."""
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
+    _args(kv, batch, q=q, sel=sel)
     if rnd.device.type != "cuda" or not rnd.is_contiguous() or rnd.element_size() != 4 or \
             rnd.dtype.is_floating_point:
         raise ValueError("rnd must be a contiguous 32-bit integer CUDA tensor")
@@ -288,8 +329,7 @@ def bounds_update(kv: PagedKV, bounds: torch.Tensor, page_ids: torch.Tensor, str
 
 def prepare_score_topk_bounds(kv: PagedKV, batch: Batch, bounds, q, topk, n_bos, n_eos, sel,
                               workspace, stream=None) -> "PreparedCall":
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
+    _args(kv, batch, q=q, sel=sel)
     _need(bounds, "bounds", kv.k_cache.dtype)
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()
@@ -310,9 +350,7 @@ def sparse_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sel: torch.T
                         sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
                         workspace: torch.Tensor, stream=None):
     """vx_sparse_paged_decode: attention over the pages listed in sel."""
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
-    _need(out, "out")
+    _args(kv, batch, q=q, sel=sel, out=out, lse=lse)
     kvs, bs = kv.struct(), batch.struct()
     _check(load_library().vx_sparse_paged_decode(
         ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), _ptr(sel), sel.shape[-1],
@@ -324,8 +362,7 @@ def full_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sm_scale: floa
                       out: torch.Tensor, lse: Optional[torch.Tensor],
                       workspace: torch.Tensor, stream=None):
     """vx_full_paged_decode: attention over every page (the dense baseline)."""
-    _need(q, "q")
-    _need(out, "out")
+    _args(kv, batch, q=q, out=out, lse=lse)
     kvs, bs = kv.struct(), batch.struct()
     _check(load_library().vx_full_paged_decode(
         ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), float(sm_scale), _ptr(out), _ptr(lse),
@@ -348,9 +385,7 @@ def sparse_decode_step_static(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: 
     """vx_sparse_decode_step_static: the decode step with the library's static
     device scratch as its workspace (no allocation; calls that overlap on one
     GPU race)."""
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
-    _need(out, "out")
+    _args(kv, batch, q=q, sel=sel, out=out, lse=lse)
     kvs, bs = kv.struct(), batch.struct()
     _check(load_library().vx_sparse_decode_step_static(
         ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos,
@@ -386,10 +421,7 @@ def paged_decode_planned(kv: PagedKV, batch: Batch, q: torch.Tensor, sel: Option
                          lse: Optional[torch.Tensor], workspace: torch.Tensor, stream=None):
     """vx_paged_decode_planned: the sparse (sel given) or dense (sel None)
     decode with an explicit plan from plan_decode."""
-    _need(q, "q")
-    _need(out, "out")
-    if sel is not None:
-        _need(sel, "sel", torch.int32)
+    _args(kv, batch, q=q, out=out, sel=sel, lse=lse)
     kvs, bs = kv.struct(), batch.struct()
     _check(load_library().vx_paged_decode_planned(
         ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), _ptr(sel),
@@ -427,8 +459,7 @@ def prepare_centroid_update(kv: PagedKV, page_ids: torch.Tensor, stream=None) ->
 
 def prepare_score_topk(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, sel, workspace,
                        stream=None) -> PreparedCall:
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
+    _args(kv, batch, q=q, sel=sel)
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()
     args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, _ptr(sel),
@@ -439,8 +470,7 @@ def prepare_score_topk(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, sel, wo
 
 def prepare_score_topk_radix(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, levels, rnd,
                              sel, workspace, stream=None) -> PreparedCall:
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
+    _args(kv, batch, q=q, sel=sel)
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()
     args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, levels, _ptr(rnd),
@@ -451,9 +481,7 @@ def prepare_score_topk_radix(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, l
 
 def prepare_sparse_paged_decode(kv: PagedKV, batch: Batch, q, sel, sm_scale, out, lse,
                                 workspace, stream=None) -> PreparedCall:
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
-    _need(out, "out")
+    _args(kv, batch, q=q, sel=sel, out=out, lse=lse)
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()
     args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), _ptr(sel), sel.shape[-1],
@@ -465,8 +493,7 @@ def prepare_sparse_paged_decode(kv: PagedKV, batch: Batch, q, sel, sm_scale, out
 
 def prepare_full_paged_decode(kv: PagedKV, batch: Batch, q, sm_scale, out, lse, workspace,
                               stream=None) -> PreparedCall:
-    _need(q, "q")
-    _need(out, "out")
+    _args(kv, batch, q=q, out=out, lse=lse)
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()
     args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), float(sm_scale), _ptr(out),
@@ -478,9 +505,7 @@ def prepare_full_paged_decode(kv: PagedKV, batch: Batch, q, sm_scale, out, lse, 
 def prepare_sparse_decode_step(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos,
                                update_completed, sm_scale, sel, out, lse, workspace,
                                stream=None) -> PreparedCall:
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
-    _need(out, "out")
+    _args(kv, batch, q=q, sel=sel, out=out, lse=lse)
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()
     args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos,
@@ -493,9 +518,7 @@ def prepare_sparse_decode_step(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos,
 def prepare_sparse_decode_step_bounds(kv: PagedKV, batch: Batch, bounds, q, topk, n_bos, n_eos,
                                       update_completed, sm_scale, sel, out, lse, workspace,
                                       stream=None) -> PreparedCall:
-    _need(q, "q")
-    _need(sel, "sel", torch.int32)
-    _need(out, "out")
+    _args(kv, batch, q=q, sel=sel, out=out, lse=lse)
     _need(bounds, "bounds", kv.k_cache.dtype)
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()

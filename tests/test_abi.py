@@ -445,3 +445,44 @@ def test_static_step_refuses_shapes_beyond_its_scratch(lib):
     for topk, bos, eos in ((-1, 1, 1), (30, -1, 1), (30, 1, 0)):
         assert step(r(kv), r(batch_struct()), FAKE, topk, bos, eos, 1, 0.1, FAKE, FAKE, FAKE,
                     None) == vx.VX_ERR_INVALID_ARGUMENT
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks dtypes, shapes and contiguity before building the
+    C structs (no GPU needed): an int64 page table would otherwise be read as
+    int32 halves, a wrong-dtype query as the cache dtype, and so on."""
+    import torch
+    P, H, S, D, B, Hq = 8, 2, 16, 64, 3, 4
+    k = torch.zeros((P, H, S, D), dtype=torch.bfloat16)
+    v = torch.zeros((P, H, S, D), dtype=torch.bfloat16)
+    cent = torch.zeros((P, H, D), dtype=torch.bfloat16)
+    kv = vx.PagedKV(k_cache=k, v_cache=v, centroids=cent)
+    pt = torch.zeros((B, 4), dtype=torch.int32)
+    sl = torch.ones(B, dtype=torch.int32)
+    bt = vx.Batch(page_table=pt, seq_lens=sl, num_q_heads=Hq, max_seq_len=64)
+    kv.struct()
+    bt.struct()
+    bad = [
+        lambda: vx.Batch(page_table=pt.long(), seq_lens=sl, num_q_heads=Hq, max_seq_len=64).struct(),
+        lambda: vx.Batch(page_table=pt, seq_lens=sl.long(), num_q_heads=Hq, max_seq_len=64).struct(),
+        lambda: vx.Batch(page_table=pt, seq_lens=sl[:2], num_q_heads=Hq, max_seq_len=64).struct(),
+        lambda: vx.Batch(page_table=pt.t(), seq_lens=torch.ones(4, dtype=torch.int32), num_q_heads=Hq,
+                         max_seq_len=64).struct(),
+        lambda: vx.PagedKV(k_cache=k, v_cache=v, centroids=cent.float()).struct(),
+        lambda: vx.PagedKV(k_cache=k, v_cache=v, centroids=cent[:4]).struct(),
+        lambda: vx.PagedKV(k_cache=k, v_cache=v.float(), centroids=cent).struct(),
+        lambda: vx.PagedKV(k_cache=k.half(), v_cache=None, centroids=None).struct(),
+        lambda: vx._args(kv, bt, q=torch.zeros((B, Hq, D), dtype=torch.float32)),
+        lambda: vx._args(kv, bt, q=torch.zeros((B, Hq + 1, D), dtype=torch.bfloat16)),
+        lambda: vx._args(kv, bt, out=torch.zeros((B, Hq, D + 1), dtype=torch.bfloat16)),
+        lambda: vx._args(kv, bt, sel=torch.zeros((B, H + 1, 5), dtype=torch.int32)),
+        lambda: vx._args(kv, bt, sel=torch.zeros((B, H, 5), dtype=torch.int64)),
+        lambda: vx._args(kv, bt, lse=torch.zeros((B, Hq), dtype=torch.bfloat16)),
+        lambda: vx._args(kv, bt, q=torch.zeros((B, D, Hq), dtype=torch.bfloat16).transpose(1, 2)),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(ValueError):
+            f()
+    vx._args(kv, bt, q=torch.zeros((B, Hq, D), dtype=torch.bfloat16),
+             out=torch.zeros((B, Hq, D), dtype=torch.bfloat16),
+             sel=torch.zeros((B, H, 5), dtype=torch.int32), lse=torch.zeros((B, Hq)))

@@ -243,7 +243,7 @@ def test_empty_batch_is_a_no_op(vx):
     bt = vx.Batch(page_table=c.pt[:0], seq_lens=c.seq_lens[:0], num_q_heads=w.num_q_heads,
                   max_seq_len=c.pt.shape[1] * w.page_size)
     ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
-    q = c.q_host.cuda()
+    q = c.q_host[:0].cuda()
     sel = torch.empty((0, w.num_kv_heads, w.k_tot), dtype=torch.int32, device="cuda")
     vx.score_topk(c.kv, bt, q, w.topk, 1, 1, sel, ws)
     out = torch.empty((0, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype, device="cuda")
