@@ -13,12 +13,17 @@ After the timed steps the same work is run once more as separate calls
 breakdown, then the dense paged decode over every page for the speedup.  All
 inputs are synthetic and seeded.
 
+The headline is the heterogeneous batch (128 requests of 4k-64k tokens, the
+largest workload); every other workload is timed after it (sparse step and
+dense decode) into the line's "configs" map.
+
 Prints one JSON line on stdout.  Progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--only]
 """
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -102,11 +107,21 @@ def centroid_bytes(w, n_pages):
 
 
 # ---------------------------------------------------------------- cpu baseline
+def host_cores():
+    """Host cores this process may use: the affinity mask, capped by
+    OMP_NUM_THREADS when the environment sets a smaller share."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and 0 < int(env) < n:
+        n = int(env)
+    return n
+
+
 def cpu_baseline(w, lay, layer, seconds, max_requests):
     """The fp64 oracle's sparse step, timed on the host on a sample of
-    requests of layer 0 (single BLAS thread)."""
+    requests of layer 0, with the BLAS thread pool on every host core this
+    process may use."""
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_limits
     import oracle as orc
     import synth
@@ -121,7 +136,8 @@ def cpu_baseline(w, lay, layer, seconds, max_requests):
         v = None if layer["V"] is None else layer["V"][idx].float().cpu().numpy()
         q = layer["q"][b].float().cpu().numpy()
         data.append((b, k, v, q))
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         cents = [orc.request_centroids(k, int(L[b]) - (1 if L[b] % w.page_size == 0 else 0),
                                        w.dtype) for b, k, v, q in data]
@@ -142,67 +158,26 @@ def cpu_baseline(w, lay, layer, seconds, max_requests):
             if el >= seconds:
                 break
     return {
-        "value": done / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{len(reqs)} of {w.batch} requests of layer 0, {done // len(reqs)} passes "
-                   f"({done} sparse decode queries: completed-page centroid, group-mean query, "
-                   f"centroid scores, exact top-k, attention over the selected pages), "
-                   f"fp64 numpy on one BLAS thread, {el:.1f} s"),
+        "value": done / el, "unit": "queries/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{w.name}: {len(reqs)} of {w.batch} requests of layer 0 at step 0, "
+                   f"{done // len(reqs)} passes ({done} sparse decode queries: completed-page "
+                   f"centroid, group-mean query, centroid scores, exact top-k, attention over "
+                   f"the selected pages), fp64 numpy with {cores} BLAS threads "
+                   f"(affinity {len(os.sched_getaffinity(0))} cores), {el:.1f} s"),
         "setup_centroids_s": setup_s,
     }
 
 
-# ---------------------------------------------------------------- main
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="qwen3_0p6b_b32_l32k")
-    ap.add_argument("--layers", type=int, default=0,
-                    help="distinct KV pools cycled over (0: enough to defeat the 256 MB cache)")
-    ap.add_argument("--dense-steps", type=int, default=40)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--cpu-requests", type=int, default=8)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--no-append", action="store_true",
-                    help="skip timing the write path (vx_append_kv)")
-    ap.add_argument("--no-bounds", action="store_true",
-                    help="skip the second summary rule (per-page key bounds)")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the multi-layer call, eager and as a replayed graph")
-    ap.add_argument("--no-radix", action="store_true",
-                    help="skip the lossy radix top-k (vx_score_topk_radix) comparison")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only copy a MIB-sized buffer a few times (reference for HBM counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library "
-              f"has no multi-GPU path: each GPU would run its own shard independently)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(args, name, full):
+    """Sets up one workload's layers and times its decode step (and, with
+    ``full``, every other section).  Returns the measurements; the workload's
+    device memory is released before returning."""
     import numpy as np
     import torch
     import block_sparse_paged_amd as vx
     import synth
 
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    if args.copy_calibration:
-        # a plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
-        # per dispatch calibrate the counters used for the roofline's traffic
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
-        return
-    vx.load_library()
-    w = synth.get_workload(args.workload)
+    w = synth.get_workload(name)
     lay = synth.build_layout(w)
     dev = torch.device("cuda:0")
     log(f"workload {w.name}: {w.description}")
@@ -615,49 +590,199 @@ def main():
                  "pct_peak": 100.0 * dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
         log(f"dense: {dense['ms_per_step']:.3f} ms/step")
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host")
-        layers[0]["q"] = layers[0]["qs"][0]
-        cpu = cpu_baseline(w, lay, layers[0], args.cpu_seconds, args.cpu_requests)
+    res = {
+        "w": w, "lay": lay, "layer0": {"K": layers[0]["K"], "V": layers[0]["V"],
+                                       "q": layers[0]["qs"][0], "pt": pt},
+        "qps": qps, "ms_per_step": ms_per_step, "max_len": max_len, "n_layers": n_layers,
+        "step_gbps": step_gbps, "achieved": achieved, "call_ms": call_ms, "b_step": b_step,
+        "step_ms": step_ms, "enqueue": enqueue, "separate": separate, "radix": radix,
+        "append": append, "bounds": bounds_sec, "graph": graph, "dense": dense,
+        "steps": K_steps,
+    }
+    return res
 
+
+def calibrate():
+    """Plain streams of known size, timed with events on the current stream:
+    device copies of 1 and 4 GiB (read + write), a gather of 64Ki random
+    4 KiB pages (the access shape of a page-table walk) and a read-only sum
+    of 4 GiB of bf16.  Under rocprofv3 --pmc their FETCH_SIZE / WRITE_SIZE
+    per dispatch give the counters' scale; timed alone they give the GPU's
+    streaming ceiling."""
+    import torch
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for gib in (1, 4):
+        n = gib << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        ms = timed(lambda: dst.copy_(src), 5)
+        out[f"copy_{gib}GiB"] = {"read_bytes": n, "write_bytes": n, "ms": ms,
+                                 "gbps": 2 * n / (ms * 1e-3) / 1e9}
+        del src, dst
+    pages = 65536
+    pool = torch.ones((4 * pages, 2048), dtype=torch.bfloat16, device="cuda")
+    idx = torch.randperm(4 * pages, device="cuda")[:pages]
+    dst = torch.empty((pages, 2048), dtype=torch.bfloat16, device="cuda")
+    ms = timed(lambda: torch.index_select(pool, 0, idx, out=dst), 5)
+    nb = pages * 4096
+    out["gather_64Ki_4KiB_pages"] = {"read_bytes": nb + 8 * pages, "write_bytes": nb, "ms": ms,
+                                     "gbps": (2 * nb + 8 * pages) / (ms * 1e-3) / 1e9}
+    del pool, dst, idx
+    x = torch.ones(2 << 30, dtype=torch.bfloat16, device="cuda")
+    ms = timed(lambda: torch.sum(x, dtype=torch.float32), 5)
+    out["read_sum_4GiB"] = {"read_bytes": 4 << 30, "write_bytes": 4, "ms": ms,
+                            "gbps": (4 << 30) / (ms * 1e-3) / 1e9}
+    torch.cuda.synchronize()
+    return out
+
+
+def config_entry(r):
+    """One workload's line in the per-workload map."""
+    d = r["dense"]
+    e = {
+        "queries_per_s": r["qps"], "ms_per_step": r["ms_per_step"],
+        "algorithmic_bytes_per_step": int(r["b_step"]),
+        "launch_ms_avg_over_timed_region": r["call_ms"],
+        "achieved_gbps": r["achieved"], "frac": r["achieved"] / HBM_PEAK_GBPS,
+        "dense_ms_per_step": d["ms_per_step"] if d else None,
+        "dense_call_ms": d["avg_call_ms"] if d else None,
+        "dense_gbps": d["gbps"] if d else None,
+        "dense_frac": d["gbps"] / HBM_PEAK_GBPS if d else None,
+        "speedup_vs_dense": (d["ms_per_step"] / r["ms_per_step"]) if d else None,
+        "steps": r["steps"],
+    }
+    return e
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="hetero_b128_l4k_64k",
+                    help="the headline workload (every section is timed on it)")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload only (no per-workload map)")
+    ap.add_argument("--config-steps", type=int, default=200,
+                    help="timed steps of each other workload in the map")
+    ap.add_argument("--config-warmup", type=int, default=20)
+    ap.add_argument("--config-dense-steps", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="distinct KV pools cycled over (0: enough to defeat the 256 MB cache)")
+    ap.add_argument("--dense-steps", type=int, default=40)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip timing the write path (vx_append_kv)")
+    ap.add_argument("--no-bounds", action="store_true",
+                    help="skip the second summary rule (per-page key bounds)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the multi-layer call, eager and as a replayed graph")
+    ap.add_argument("--no-radix", action="store_true",
+                    help="skip the lossy radix top-k (vx_score_topk_radix) comparison")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only time plain streams of known size (copies, a page gather, a "
+                         "read-only sum): the streaming ceiling, and the references that "
+                         "scale rocprofv3's HBM counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library "
+              f"has no multi-GPU path: each GPU would run its own shard independently)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import block_sparse_paged_amd as vx
+    import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    if args.calibrate:
+        print(json.dumps(calibrate()), flush=True)
+        return
+    vx.load_library()
+    names = [args.workload]
+    if not args.only:
+        names += [n for n in synth.WORKLOADS if n != args.workload]
+    configs = {}
+    head = None
+    cpu = None
+    for i, name in enumerate(names):
+        full = i == 0
+        sub = args if full else argparse.Namespace(**{
+            **vars(args), "no_radix": True, "no_append": True, "no_bounds": True,
+            "no_graph": True, "steps": args.config_steps, "warmup": args.config_warmup,
+            "dense_steps": args.config_dense_steps, "layers": 0})
+        r = run_workload(sub, name, full)
+        configs[name] = config_entry(r)
+        if full:
+            head = {k: v for k, v in r.items() if k != "layer0"}
+            if not args.no_cpu_baseline:
+                log("timing the oracle on the host")
+                cpu = cpu_baseline(r["w"], r["lay"], r["layer0"], args.cpu_seconds,
+                                   args.cpu_requests)
+        del r
+        gc.collect()
+        torch.cuda.empty_cache()
+
+    w, r = head["w"], head
+    dense = r["dense"]
     line = {
         "metric": METRIC,
-        "value": qps,
+        "value": r["qps"],
         "unit": "queries/s",
         "n_gpus": 1,
-        "steps": K_steps,
-        "warmup": W_steps,
-        "ms_per_step": ms_per_step,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "seq_len": int(max_len),
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": int(r["max_len"]),
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
                    "page_size": w.page_size, "topk": w.topk, "n_bos": w.n_bos,
-                   "n_eos": w.n_eos, "layers_cycled": n_layers},
-        "achieved_gbps": step_gbps,
-        "pct_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
-        "speedup_vs_dense": (dense["ms_per_step"] / ms_per_step) if dense else None,
+                   "n_eos": w.n_eos, "layers_cycled": r["n_layers"]},
+        "achieved_gbps": r["step_gbps"],
+        "pct_peak": 100.0 * r["step_gbps"] / HBM_PEAK_GBPS,
+        "speedup_vs_dense": (dense["ms_per_step"] / r["ms_per_step"]) if dense else None,
         "roofline": {"bound": "hbm", "kernel": "vx_sparse_decode_step",
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name),
+                     "achieved": r["achieved"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": r["achieved"] / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)"},
         "cpu_baseline": cpu,
-        "algorithmic_bytes_per_step": int(b_step),
-        "launch_ms_avg_over_timed_region": call_ms,
-        "launch_ms_p10_p50_p90_with_events": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
-        "host_enqueue_us_per_step": enqueue * 1e6 / K_steps,
-        "separate_calls": separate,
-        "radix_topk": radix,
-        "append_kv": append,
-        "page_bounds": bounds_sec,
-        "decode_layers": graph,
+        "algorithmic_bytes_per_step": int(r["b_step"]),
+        "launch_ms_avg_over_timed_region": r["call_ms"],
+        "launch_ms_p10_p50_p90_with_events": [float(np.percentile(r["step_ms"], p))
+                                              for p in (10, 50, 90)],
+        "host_enqueue_us_per_step": r["enqueue"] * 1e6 / args.steps,
+        "separate_calls": r["separate"],
+        "radix_topk": r["radix"],
+        "append_kv": r["append"],
+        "page_bounds": r["bounds"],
+        "decode_layers": r["graph"],
         "dense": dense,
+        "configs": configs,
     }
     print(json.dumps(line), flush=True)
 

@@ -66,7 +66,8 @@ class DecodePlanStruct(ctypes.Structure):
     _fields_ = [
         ("op", ctypes.c_int32), ("num_cus", ctypes.c_int32),
         ("pages_per_split", ctypes.c_int32), ("n_split", ctypes.c_int32),
-        ("reserved_", ctypes.c_int32 * 2), ("workspace_bytes", ctypes.c_uint64),
+        ("work_list", ctypes.c_int32), ("blocks", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_uint64),
     ]
 
 

@@ -125,9 +125,19 @@ int max_pages_eff(const vx_paged_kv* kv, const vx_batch* bt) {
 struct DecodePlan {
   int pages_per_split = 1;
   int n_split = 1;
+  bool work_list = false;  // dense: persistent blocks over (request, chunk, KV head) items
+  int blocks = 0;          // blocks of a work-list launch
   size_t part_o_bytes = 0, part_ml_bytes = 0;
   size_t ws_bytes() const { return part_o_bytes + part_ml_bytes; }
 };
+
+// Dense work list: pages per item, and blocks per CU.  One 8-wave block is
+// resident per CU at a time (registers); four per CU in all still leave the
+// dispatcher room to even out CUs that run at different speeds.  Items of
+// 64 to 512 pages and 2 to 8 blocks per CU measured within 3% of each other
+// (Qwen-like, heterogeneous and long-context dense decodes).
+constexpr int kItemPages = 128;
+constexpr int kItemBlocksPerCU = 4;
 
 // Splits for `pages` pages per (request, KV head) on a GPU of `cus` compute
 // units.  pps_hint > 0 asks for that many pages per split (still at least
@@ -141,7 +151,16 @@ DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, boo
   pages = std::max(pages, 1);
   cus = std::max(cus, 1);
   int pps;
-  if (pps_hint > 0) {
+  if (!sparse && !is_mla(kv) && bt->batch <= decode_items_max_batch()) {
+    // dense: equal-size items over every request's pages, walked by a fixed
+    // number of blocks, so a mixed-length batch streams evenly
+    pps = std::max(pps_hint > 0 ? pps_hint : kItemPages, ceil_div(pages, kMaxSplits));
+    p.work_list = true;
+    p.pages_per_split = pps;
+    p.n_split = ceil_div(pages, pps);
+    const long long items = units * p.n_split;
+    p.blocks = (int)std::min<long long>(items, (long long)cus * kItemBlocksPerCU);
+  } else if (pps_hint > 0) {
     pps = pps_hint;
   } else if (is_mla(kv)) {
     const long long target = (long long)cus * (sparse ? kMlaSparseBlocksPerCU : kMlaFullBlocksPerCU);
@@ -164,10 +183,12 @@ DecodePlan plan_decode(const vx_paged_kv* kv, const vx_batch* bt, int pages, boo
            (double)ceil_div(pages, pps) * G * (kv->head_dim_v + 2) * 8 > 0.15 * kv_bytes)
       ++pps;
   }
-  pps = std::max(pps, ceil_div(pages, kMaxSplits));
-  if (is_mla(kv)) pps = std::min(pps, mla_max_pages_per_split());   // LDS page list
-  p.pages_per_split = pps;
-  p.n_split = ceil_div(pages, pps);
+  if (!p.work_list) {
+    pps = std::max(pps, ceil_div(pages, kMaxSplits));
+    if (is_mla(kv)) pps = std::min(pps, mla_max_pages_per_split());   // LDS page list
+    p.pages_per_split = pps;
+    p.n_split = ceil_div(pages, pps);
+  }
   if (p.n_split > 1) {
     const size_t rows = (size_t)bt->batch * bt->num_q_heads * p.n_split;
     p.part_o_bytes = align_up(rows * kv->head_dim_v * sizeof(float));
@@ -242,12 +263,21 @@ vx_status run_decode(const vx_paged_kv* kv, const vx_batch* bt, const void* q,
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_o_bytes);
   }
+  a.work_list = p.work_list ? 1 : 0;
   const int G = bt->num_q_heads / kv->num_kv_heads;
-  hipError_t e = is_mla(kv) ? launch_decode_mla(a, stream)
-                            : launch_decode_split(kv->dtype, kv->head_dim_qk, G, a, stream);
+  hipError_t e =
+      p.work_list ? launch_decode_items(kv->dtype, kv->head_dim_qk, G, a, p.blocks, stream)
+      : is_mla(kv) ? launch_decode_mla(a, stream)
+                   : launch_decode_split(kv->dtype, kv->head_dim_qk, G, a, stream);
   if (e != hipSuccess) return VX_ERR_HIP;
   if (p.n_split > 1) {
     CombineArgs c{};
+    if (p.work_list) {         // a request merges only the chunks it has
+      c.seq_lens = bt->seq_lens;
+      c.S_p = kv->page_size;
+      c.pages_per_split = p.pages_per_split;
+      c.max_tokens = bt->max_seq_len;
+    }
     c.part_o = a.part_o;
     c.part_ml = a.part_ml;
     c.out = out;
@@ -972,6 +1002,8 @@ vx_status vx_plan_decode(int32_t op, const vx_paged_kv* kv, const vx_batch* batc
   plan->num_cus = cus;
   plan->pages_per_split = p.pages_per_split;
   plan->n_split = p.n_split;
+  plan->work_list = p.work_list ? 1 : 0;
+  plan->blocks = p.blocks;
   plan->workspace_bytes = p.ws_bytes();
   return VX_OK;
 }
@@ -989,8 +1021,9 @@ vx_status vx_paged_decode_planned(const vx_paged_kv* kv, const vx_batch* batch, 
   if (st != VX_OK) return st;
   // the plan must be one vx_plan_decode made for these shapes
   if (again.num_cus != plan->num_cus || again.pages_per_split != plan->pages_per_split ||
-      again.n_split != plan->n_split || again.workspace_bytes != plan->workspace_bytes ||
-      plan->reserved_[0] != 0 || plan->reserved_[1] != 0 || (sparse != (sel != nullptr)))
+      again.n_split != plan->n_split || again.work_list != plan->work_list ||
+      again.blocks != plan->blocks || again.workspace_bytes != plan->workspace_bytes ||
+      (sparse != (sel != nullptr)))
     return VX_ERR_INVALID_ARGUMENT;
   if (!(sm_scale > 0.f) || sm_scale == __builtin_inff()) return VX_ERR_INVALID_ARGUMENT;
   if (batch->batch == 0) return VX_OK;
@@ -1000,6 +1033,8 @@ vx_status vx_paged_decode_planned(const vx_paged_kv* kv, const vx_batch* batch, 
   DecodePlan p;
   p.pages_per_split = plan->pages_per_split;
   p.n_split = plan->n_split;
+  p.work_list = plan->work_list != 0;
+  p.blocks = plan->blocks;
   if (p.n_split > 1) {
     const size_t rows = (size_t)batch->batch * batch->num_q_heads * p.n_split;
     p.part_o_bytes = align_up(rows * kv->head_dim_v * sizeof(float));

@@ -118,6 +118,81 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// K4, dense work list: the dense decode of a batch whose requests differ in
+// length ("workload planner for balanced GPU scheduling", Vortex article,
+// "A dual-stage programmable abstraction").  Every request's pages are cut
+// into chunks of pages_per_split pages; an item is one (request, chunk, KV
+// head), all items but each request's last of equal size.  A fixed number of
+// persistent blocks take items blockIdx.x, blockIdx.x + gridDim.x, ... in
+// (request, chunk, head) order, so every block streams the same number of
+// bytes to within one item, whatever the length mix.  Each block first
+// forms the chunk offsets of every request itself (a block scan over the
+// lengths), so the launch needs no host synchronisation, no counters and no
+// cleared memory.  Chunk c of a request is its split c: the partials land in
+// the split-K layout and combine_kernel merges each request's own chunks.
+constexpr int kItemsMaxBatch = 2048;       // LDS: chunk offsets and lengths (16 KiB)
+// Waves per work-list block.  Measured against 4-wave blocks (two resident
+// per CU): the 8-wave block streams as fast on uniform batches and faster on
+// mixed ones.
+constexpr int kItemWaves = 8;
+
+template <typename T, int D, int G, int HS, int PF, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_items_kernel(DecodeArgs a) {
+  constexpr int NT = NW * 64;
+  extern __shared__ int sh[];                // coff [B + 1], then seq [B]
+  __shared__ int wsum[NT / 64];
+  int* coff = sh;
+  int* sq = sh + a.B + 1;
+  const int tid = threadIdx.x;
+  const int C = a.pages_per_split;
+  int run = 0;
+  for (int base = 0; base < a.B; base += NT) {
+    const int i = base + tid;
+    int n = 0;
+    if (i < a.B) {
+      int seq = a.seq_lens[i];
+      seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
+      sq[i] = seq;
+      const int n_b = (seq + a.S_p - 1) / a.S_p;
+      n = max((n_b + C - 1) / C, 1);           // an empty request still gets its (empty) item
+    }
+    int tot;
+    const int ex = block_exclusive_scan<NT>(n, wsum, &tot);
+    if (i < a.B) coff[i] = run + ex;
+    run += tot;
+    __syncthreads();                          // wsum is reused by the next round
+  }
+  if (tid == 0) coff[a.B] = run;
+  __syncthreads();
+  const int total = run * a.H_kv;
+  int b = 0;
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int cidx = item / a.H_kv, h = item - cidx * a.H_kv;
+    while (coff[b + 1] <= cidx) ++b;           // items ascend, so b only moves forward
+    const int chunk = cidx - coff[b];
+    const int seq = sq[b];
+    const int n_b = (seq + a.S_p - 1) / a.S_p;
+    const int p0 = chunk * C, p1 = min(p0 + C, n_b);
+    const int32_t* ptb = a.pt + (size_t)b * a.pt_stride;
+    auto page_at = [&](int idx, bool active) -> int2 {
+      return make_int2(idx, active ? ptb[idx] : 0);
+    };
+    attend_pages<T, D, G, HS, PF, NW>(a, b, h, chunk, p0, p1, seq, page_at);
+    __syncthreads();                          // the merge's LDS is free for the next item
+  }
+}
+
+// Splits row (b, .) of a combine merges: all n_split, or, for the work list,
+// the chunks request b has.
+__device__ __forceinline__ int combine_splits(const CombineArgs& a, size_t row) {
+  if (!a.seq_lens) return a.n_split;
+  const int b = (int)(row / a.H_q);
+  int seq = a.seq_lens[b];
+  seq = seq < 0 ? 0 : (seq > a.max_tokens ? a.max_tokens : seq);
+  const int n_b = (seq + a.S_p - 1) / a.S_p;
+  return min(max((n_b + a.pages_per_split - 1) / a.pages_per_split, 1), a.n_split);
+}
+
 // K5: merge the splits of one (request, query head).  Splits with an empty
 // page range have sum 0 and are skipped.  256 threads per row; each thread
 // owns D_v/256 output dims (at least one) and keeps eight splits' loads in
@@ -131,9 +206,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   __shared__ float red[kCombineThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = blockIdx.x;            // b * H_q + hq
+  const int n = combine_splits(a, row);
   const float* ml = a.part_ml + row * a.n_split * 2;
   float mx = -INFINITY;
-  for (int i = tid; i < a.n_split; i += kCombineThreads)
+  for (int i = tid; i < n; i += kCombineThreads)
     if (ml[2 * i + 1] > 0.f) mx = fmaxf(mx, ml[2 * i]);
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
@@ -143,7 +219,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   for (int v = 1; v < kCombineThreads / 64; ++v) mx = fmaxf(mx, red[v]);
   __syncthreads();
   float tot = 0.f;
-  for (int i = tid; i < a.n_split; i += kCombineThreads) {
+  for (int i = tid; i < n; i += kCombineThreads) {
     const float li = ml[2 * i + 1];
     const float wi = li > 0.f ? exp2f(ml[2 * i] - mx) : 0.f;
     w[i] = wi;
@@ -159,19 +235,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   const float* po = a.part_o + row * a.n_split * DV;
-  for (int i0 = 0; i0 < a.n_split; i0 += 8) {
+  for (int i0 = 0; i0 < n; i0 += 8) {
     float x[8][PER];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int d = j * kCombineThreads + tid;
-        x[u][j] = (i0 + u < a.n_split && d < DV && w[i0 + u] != 0.f)
+        x[u][j] = (i0 + u < n && d < DV && w[i0 + u] != 0.f)
                       ? po[(size_t)(i0 + u) * DV + d] : 0.f;
       }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (i0 + u < a.n_split) {
+      if (i0 + u < n) {
         const float wi = w[i0 + u];
 #pragma unroll
         for (int j = 0; j < PER; ++j) acc[j] = fmaf(wi, x[u][j], acc[j]);
@@ -202,9 +278,10 @@ __global__ __launch_bounds__(64) void combine_few_kernel(CombineArgs a) {
   static_assert(PD * 64 == DV, "rows of a multiple of 64 dims");
   const int lane = threadIdx.x;
   const size_t row = blockIdx.x;            // b * H_q + hq
-  const int n = a.n_split;
-  const float2 mli = *reinterpret_cast<const float2*>(a.part_ml + (row * n + min(lane, n - 1)) * 2);
-  const float* po = a.part_o + row * n * DV + lane * PD;
+  const int ns = a.n_split;                 // row stride of the partials
+  const int n = combine_splits(a, row);     // splits this row merges
+  const float2 mli = *reinterpret_cast<const float2*>(a.part_ml + (row * ns + min(lane, n - 1)) * 2);
+  const float* po = a.part_o + row * ns * DV + lane * PD;
   float x[kCombineFew][PD];
 #pragma unroll
   for (int i = 0; i < kCombineFew; ++i) {
@@ -261,6 +338,26 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int G>
+hipError_t run_items(const DecodeArgs& a, int blocks, hipStream_t s) {
+  constexpr int HS = attend_head_slices<G>(), PF = attend_prefetch<T, D>();
+  const size_t lds = (2 * (size_t)a.B + 1) * sizeof(int);
+  hipLaunchKernelGGL((decode_items_kernel<T, D, G, HS, PF, kItemWaves>), dim3(blocks),
+                     dim3(kItemWaves * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run_items_g(int G, const DecodeArgs& a, int blocks, hipStream_t s) {
+  switch (G) {
+    case 1: return run_items<T, D, 1>(a, blocks, s);
+    case 2: return run_items<T, D, 2>(a, blocks, s);
+    case 4: return run_items<T, D, 4>(a, blocks, s);
+    case 8: return run_items<T, D, 8>(a, blocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int D>
 hipError_t run_decode_g(int G, const DecodeArgs& a, hipStream_t s) {
   switch (G) {
@@ -290,6 +387,23 @@ hipError_t launch_decode_split(int dtype, int D, int G, const DecodeArgs& a, hip
   } else {
     if (D == 64) return run_decode_g<bf16_t, 64>(G, a, s);
     if (D == 128) return run_decode_g<bf16_t, 128>(G, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int decode_items_max_batch() { return kItemsMaxBatch; }
+
+hipError_t launch_decode_items(int dtype, int D, int G, const DecodeArgs& a, int blocks,
+                               hipStream_t s) {
+  if (a.B > kItemsMaxBatch || a.B < 1 || blocks < 1 || a.pages_per_split < 1 || a.sel ||
+      a.scores)
+    return hipErrorInvalidValue;
+  if (dtype == 0) {
+    if (D == 64) return run_items_g<float, 64>(G, a, blocks, s);
+    if (D == 128) return run_items_g<float, 128>(G, a, blocks, s);
+  } else {
+    if (D == 64) return run_items_g<bf16_t, 64>(G, a, blocks, s);
+    if (D == 128) return run_items_g<bf16_t, 128>(G, a, blocks, s);
   }
   return hipErrorInvalidValue;
 }

@@ -71,6 +71,10 @@ struct DecodeArgs {
   float* lse;             // [B, H_q] or nullptr (direct mode)
   int32_t B, H_q, H_kv, S_p, pt_stride, k_tot, max_tokens;
   int32_t pages_per_split, n_split;
+  // work list (dense calls): the launch's blocks walk (request, chunk of
+  // pages_per_split pages, KV head) items in turn instead of one block per
+  // (split, KV head, request); chunk c of a request is its split c
+  int32_t work_list;
   int32_t v_stride_tok;   // elements between consecutive tokens of V (D_qk when aliased)
   float scale_log2;       // sm_scale * log2(e)
   // Selection in the decode kernel (scores != nullptr): every split block of
@@ -103,6 +107,11 @@ struct CombineArgs {
   void* out;
   float* lse;
   int32_t B, H_q, n_split, D_v;
+  // when set, row (b, .) merges only the splits request b has:
+  // ceil(ceil(seq / S_p) / pages_per_split), at least 1 (the others were
+  // never written)
+  const int32_t* seq_lens;
+  int32_t S_p, pages_per_split, max_tokens;
 };
 
 hipError_t launch_centroid(int dtype, const CentroidArgs& a, hipStream_t s);
@@ -148,6 +157,12 @@ hipError_t launch_indexer_fused(int dtype, const ScoreArgs& a, const TopkArgs& t
                                 bool bounds = false);
 // D = D_qk = D_v for this path; G = H_q / H_kv.
 hipError_t launch_decode_split(int dtype, int D, int G, const DecodeArgs& a, hipStream_t s);
+// The dense work list: `blocks` persistent blocks over every (request,
+// chunk, KV head) item (a.work_list set, a.sel and a.scores null).  LDS
+// bound on B: decode_items_max_batch().
+hipError_t launch_decode_items(int dtype, int D, int G, const DecodeArgs& a, int blocks,
+                               hipStream_t s);
+int decode_items_max_batch();
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 // Whether the MLA decode can select its pages itself (scores given) for this
 // score row length and selection size.

@@ -264,7 +264,11 @@ vx_status vx_sparse_paged_decode(const vx_paged_kv* kv, const vx_batch* batch,
 /* Full paged attention over every page of every request: the baseline
  * (README, "Using Your Sparse Attention with SGLang": with sparsity off, or
  * for a skipped layer, full attention is used).  Same definition as
- * vx_sparse_paged_decode with sel = all n_b pages.
+ * vx_sparse_paged_decode with sel = all n_b pages.  Scheduled as a work list
+ * (the article's "workload planner for balanced GPU scheduling"): every
+ * request's pages are cut into equal 128-page items that a fixed number of
+ * blocks walk, so requests of mixed lengths stream evenly; the item offsets
+ * come from seq_lens on the device, without a host synchronisation.
  *   workspace  at least vx_workspace_size(VX_OP_FULL_DECODE, ...) bytes */
 vx_status vx_full_paged_decode(const vx_paged_kv* kv, const vx_batch* batch,
                                const void* q, float sm_scale, void* out, float* lse,
@@ -385,7 +389,11 @@ typedef struct {
   int32_t num_cus;          /* compute units the plan was made for               */
   int32_t pages_per_split;  /* list entries one split attends                    */
   int32_t n_split;          /* splits per (request, KV head); 1: direct output   */
-  int32_t reserved_[2];     /* 0                                                 */
+  int32_t work_list;        /* 1: a fixed number of blocks walk the (request,
+                               split, KV head) items of the whole batch, the
+                               dense calls' balanced schedule; 0: one block per
+                               (split, KV head, request)                       */
+  int32_t blocks;           /* blocks of a work-list launch, else 0              */
   uint64_t workspace_bytes; /* workspace the planned call needs                  */
 } vx_decode_plan;
 
@@ -393,8 +401,11 @@ typedef struct {
  * VX_OP_SPARSE_DECODE only) on a GPU of `num_cus` compute units (0: the
  * current device's), with `pages_per_split` pages per split (0: the
  * planner's choice; a given value is raised to ceil(pages / 1024) and, for
- * MLA shapes, capped at 256).  Host-only and a pure function of its
- * arguments (and, for num_cus 0, of the device's CU count); writes *plan. */
+ * MLA shapes, capped at 256).  Dense plans of D_qk 64 / 128 with up to 2048
+ * requests are work lists of pages_per_split-page items (128 by default);
+ * other plans have one block per (split, KV head, request).  Host-only and a
+ * pure function of its arguments (and, for num_cus 0, of the device's CU
+ * count); writes *plan. */
 vx_status vx_plan_decode(int32_t op, const vx_paged_kv* kv, const vx_batch* batch, int32_t k_tot,
                          int32_t num_cus, int32_t pages_per_split, vx_decode_plan* plan /* host */);
 

@@ -249,10 +249,13 @@ def test_plan_is_a_function_of_shapes_and_cus(lib, cus):
     bt2 = batch_struct(batch=32, num_q_heads=16, max_pages_per_req=2048, max_seq_len=32768)
     st, p = plan(lib, vx.VX_OP_SPARSE_DECODE, kv, bt2, 32, cus)
     assert st == 0 and p.n_split == 1 and p.workspace_bytes == 0
-    # dense: 2048 pages over ceil(16 cus / 256) splits, at least 64 pages each
+    # dense: the work list of 128-page items (16 per request and KV head),
+    # walked by four blocks per CU
     st, p = plan(lib, vx.VX_OP_FULL_DECODE, kv, bt2, 0, cus)
-    n_want = -(-16 * cus // 256)
-    assert st == 0 and p.pages_per_split == max(-(-2048 // n_want), 64)
+    assert st == 0 and p.work_list == 1 and p.pages_per_split == 128 and p.n_split == 16
+    assert p.blocks == min(32 * 8 * 16, 4 * cus)
+    rows = 32 * 16 * 16
+    assert p.workspace_bytes == -(-rows * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
     # the same shapes always give the same plan
     assert plan(lib, vx.VX_OP_FULL_DECODE, kv, bt2, 0, cus)[1].pages_per_split == p.pages_per_split
 
@@ -266,7 +269,12 @@ def test_plan_with_a_fixed_split_size(lib):
     st, p2 = plan(lib, vx.VX_OP_SPARSE_DECODE, kv, bt, 32, 256, 1000)
     assert st == 0 and p2.n_split == 1 and p2.workspace_bytes == 0     # one split: direct output
     st, p3 = plan(lib, vx.VX_OP_FULL_DECODE, kv, bt, 0, 256, 0)
-    assert st == 0 and p3.pages_per_split >= 64
+    assert st == 0 and p3.pages_per_split == 128 and p3.work_list == 1 and p3.n_split == 2
+    st, p4 = plan(lib, vx.VX_OP_FULL_DECODE, kv, bt, 0, 256, 7)       # a fixed item size
+    assert st == 0 and p4.pages_per_split == 7 and p4.n_split == 37 and p4.blocks == 2 * 8 * 37
+    big = batch_struct(batch=4096, max_pages_per_req=64, max_seq_len=1024)
+    st, p5 = plan(lib, vx.VX_OP_FULL_DECODE, kv, big, 0, 256, 0)
+    assert st == 0 and p5.work_list == 0                                # beyond the list's batch bound
     r = ctypes.byref
     for bad in ((vx.VX_OP_SCORE_TOPK, 32, 256, 0), (vx.VX_OP_SPARSE_DECODE, 0, 256, 0),
                 (vx.VX_OP_SPARSE_DECODE, 32, -1, 0), (vx.VX_OP_SPARSE_DECODE, 32, 256, -2)):

@@ -828,3 +828,52 @@ def test_device_centroid_shortcut(vx, name):
         assert np.array_equal(np.isnan(got), np.isnan(want))
         m = ~np.isnan(want)
         assert np.array_equal(got[m], want[m]), f"request {b}"
+
+
+# ---------------------------------------------------------------- dense work list
+@pytest.mark.parametrize("dtype,D,G,S", [("bf16", 128, 4, 16), ("f32", 64, 1, 64),
+                                         ("bf16", 64, 8, 16)])
+@pytest.mark.parametrize("pps", [0, 3, 16])
+def test_dense_work_list_ragged(vx, dtype, D, G, S, pps):
+    """The dense decode's work list over requests of very different lengths
+    (one token to a few thousand pages, partial last pages), with the
+    planner's item size and with small forced items, so that items end at
+    every kind of page boundary and requests own 1 to hundreds of items:
+    every request's output equals the oracle's full attention."""
+    lens = (1, S - 1, S, S + 1, 37 * S + 3, 230 * S, 257 * S + 9, 2 * S + 1, 129 * S)
+    w = synth.Workload(name="ragged_dense", batch=len(lens), num_q_heads=2 * G, num_kv_heads=2,
+                       head_dim_qk=D, head_dim_v=D, page_size=S, dtype=dtype, topk=4,
+                       structure="page_offset", seed=88, seq_lens=lens, spare_pages=3)
+    H.log(f"case {H.describe(w)} pages_per_split={pps}")
+    c = H.setup_case(vx, w)
+    bt = c.batch(vx)
+    plan = vx.plan_decode(vx.VX_OP_FULL_DECODE, c.kv, bt, 0, 0, pps)
+    assert plan.work_list == 1 and (pps == 0 or plan.pages_per_split == pps)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim_v), float("nan"), dtype=w.torch_dtype,
+                     device="cuda")
+    lse = torch.full((w.batch, w.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    q = c.q_host.cuda()
+    vx.paged_decode_planned(c.kv, bt, q, None, plan, w.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        _check_request(vx, c, b, None, out, lse, sparse=False)
+
+
+def test_dense_beyond_work_list_batch(vx):
+    """More requests than the work list takes (2048): the dense decode plans
+    one block per (split, KV head, request) instead, and still equals the
+    oracle (sampled requests)."""
+    rng = np.random.default_rng(90)
+    lens = tuple(int(x) for x in rng.integers(1, 90, size=2100))
+    w = synth.Workload(name="wide_dense", batch=len(lens), num_q_heads=2, num_kv_heads=1,
+                       head_dim_qk=128, head_dim_v=128, page_size=16, dtype="bf16", topk=2,
+                       structure="page_offset", seed=90, seq_lens=lens, spare_pages=3)
+    H.log(f"case {H.describe(w)}")
+    c = H.setup_case(vx, w)
+    bt = c.batch(vx)
+    assert vx.plan_decode(vx.VX_OP_FULL_DECODE, c.kv, bt).work_list == 0
+    out, lse = H.run_full(vx, c, c.q_host.cuda())
+    torch.cuda.synchronize()
+    for b in (0, 1, 777, 2047, 2048, 2099):
+        _check_request(vx, c, b, None, out, lse, sparse=False)
