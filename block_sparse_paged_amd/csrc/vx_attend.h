@@ -119,14 +119,14 @@ __device__ __forceinline__ void attend_pages_valu(const DecodeArgs& a, int b, in
 #pragma unroll
         for (int i = 1; i < NL; ++i) mc = fmaxf(mc, s[g][i]);
         const float mn = fmaxf(m[g], mc);
-        const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[g] - mn);
+        const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m[g] - mn);
         m[g] = mn;
         l[g] *= alpha;
 #pragma unroll
         for (int e = 0; e < E; ++e) o[g][e] *= alpha;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-          const float p = (mn == -INFINITY) ? 0.f : exp2f(s[g][i] - mn);
+          const float p = (mn == -INFINITY) ? 0.f : fast_exp2(s[g][i] - mn);
           s[g][i] = p;
           l[g] += p;
         }
@@ -344,12 +344,16 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
       for (int ks = 0; ks < KS; ++ks)
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kd[ks]), qB[ks], sc,
                                                     0, 0, 0);
-      float sv[4], cm = -INFINITY;
+      // raw scores; masked only where the chunk reaches past seq (the same
+      // in every lane); the scale is positive, so the maximum is taken
+      // before scaling
+      float sv[4] = {sc[0], sc[1], sc[2], sc[3]};
+      if (tok0 + kChunk > seq) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = tok0 + 4 * lg + i < seq ? sc[i] * a.scale_log2 : -INFINITY;
-        cm = fmaxf(cm, sv[i]);
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + 4 * lg + i >= seq) sv[i] = -INFINITY;
       }
+      float cm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       {
         const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(cm), __float_as_uint(cm),
                                                           false, false);
@@ -358,14 +362,22 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
                                                           false, false);
         cm = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
       }
-      const float mn = fmaxf(m, cm);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-      m = mn;
+      cm *= a.scale_log2;
+      // lazy reference (kLazyRescale): o and l are rescaled only when a
+      // head's maximum passes its reference by more than the margin
+      float alpha = 1.f;
+      const bool grow = __ballot(cm > m + kLazyRescale) != 0ull;
+      if (grow) {
+        const float mn = fmaxf(m, cm);
+        alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+        m = mn;
+      }
+      const float neg_m = (m == -INFINITY) ? 0.f : -m;
       s16x4 pB;
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = (mn == -INFINITY) ? 0.f : exp2f(sv[i] - mn);
+        const float p = fast_exp2(fmaf(sv[i], a.scale_log2, neg_m));
         ps += p;                          // the denominator keeps fp32 weights
         pB[i] = (short)f32_to_bf16(p);
       }
@@ -377,7 +389,13 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
                                                           false, false);
         ps = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
       }
-      l = l * alpha + ps;
+      l = grow ? l * alpha + ps : l + ps;
+      if (grow) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[dt][i] *= alpha;
+      }
       // the wave's V rows are in LDS before its transposing reads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -386,10 +404,7 @@ __device__ __forceinline__ void attend_pages_mfma(const DecodeArgs& a, int b, in
       for (int dt = 0; dt < DT; ++dt) {
         const s16x4 vA = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(vbuf + tr_off + 32 * dt));
-        f32x4 acc = o[dt];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pB, acc, 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pB, o[dt], 0, 0, 0);
       }
     };
 #pragma unroll

@@ -247,26 +247,37 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
       }
     }
     // ---- online softmax of head hl over the tile's tokens 8(i/4) + 4hh + i%4
-    float mx = neg_inf();
+    // (the scale is positive, so the maximum is taken on the unscaled scores;
+    // masking only where the tile reaches past seq, the same in every lane)
+    if (tok0 + kT > seq) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int pos = tok0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      sv[i] = pos < seq ? sv[i] * a.scale_log2 : neg_inf();
-      mx = fmaxf(mx, sv[i]);
+      for (int i = 0; i < 16; ++i)
+        if (tok0 + 8 * (i >> 2) + 4 * hh + (i & 3) >= seq) sv[i] = neg_inf();
     }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
     {
       const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                         false, false);
       mx = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
     }
-    const float m_new = fmaxf(m, mx);
-    const float alpha = (m_new == neg_inf()) ? 1.f : exp2f(m - m_new);
-    m = m_new;
+    mx *= a.scale_log2;
+    // lazy reference: O and lsum are rescaled only when a head's maximum
+    // passes its reference by more than kLazyRescale (always on the first tile)
+    float alpha = 1.f;
+    const bool grow = __ballot(mx > m + kLazyRescale) != 0ull;
+    if (grow) {
+      const float m_new = fmaxf(m, mx);
+      alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+    }
+    const float neg_m = (m == neg_inf()) ? 0.f : -m;
     s16x8 pk[2];
     float ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = (m_new == neg_inf()) ? 0.f : exp2f(sv[i] - m_new);
+      const float p = fast_exp2(fmaf(sv[i], a.scale_log2, neg_m));
       ps += p;
       pk[i >> 3][i & 7] = (short)f32_to_bf16(p);
     }
@@ -275,14 +286,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
                                                         false, false);
       ps = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
     }
-    lsum = lsum * alpha + ps;
+    lsum = grow ? lsum * alpha + ps : lsum + ps;
 
     // ---- O^T += V^T P^T over the tile's two 16-token slices
+    if (grow) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       f32x16 acc = o[dt];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] *= alpha;
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
         const uint8_t* vsrc = ktile + (16 * sl + tr_row) * kLdsRow + 2 * (128 * w + 32 * dt + tr_col);

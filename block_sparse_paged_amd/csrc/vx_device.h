@@ -54,6 +54,19 @@ template <> struct Vec16<bf16_t> {
   __device__ __forceinline__ static bf16_t from_f32(float x) { return f32_to_bf16(x); }
 };
 
+// 2^x on the hardware exponential (v_exp_f32): results below the smallest
+// normal float flush to 0, and 2^-inf is 0.  Softmax weights that small carry
+// nothing, so the attention softmaxes use it instead of exp2f, whose
+// subnormal range reduction costs three more instructions per call.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online softmax with a lazy reference: the running output and denominator
+// are rescaled only when some head's maximum logit (log2 units) rises more
+// than this above the reference they share; below it the weights exp2(s -
+// reference) stay under 2^kLazyRescale, and the final output o / l is the
+// same softmax whatever the reference.
+constexpr float kLazyRescale = 8.f;
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
