@@ -7,23 +7,28 @@
 //
 // At ~60 flop per byte of KV this is past the fp32 VALU roofline, so both
 // products run on gfx950 matrix cores (fp32 accumulation).  One 256-thread
-// block per (split, request); per 32-token tile (36 KiB), three barriers:
-//   - all threads copy the tile HBM -> registers -> LDS, the next tile's
-//     global loads being in flight while the current one is computed;
-//   - S^T[32 tokens x 32 heads] = K Q^T on mfma_f32_32x32x16_bf16, each wave
-//     over its own 144 of the 576 dims (its query slice stays in registers);
-//     the four partial products meet in LDS and every wave adds them in wave
-//     order, so each wave holds the whole S^T;
-//   - the online softmax of the 32 heads then needs no exchange: a lane holds
-//     16 tokens of one head, the other 16 sit in the lane 32 apart;
-//   - O^T[dims x heads] += V^T P^T on the same MFMA: wave w owns V dims
-//     128w .. 128w+127 (4 tiles of 32); P is already in the B operand layout
-//     in registers; V^T is read from the K tile in LDS (so HBM sees each
-//     576-dim row once) with the transposing 64-bit LDS read.
+// block per (split, request); 32-token tiles (36 KiB) staged HBM -> registers
+// -> LDS, two tile buffers, the next tile's global loads in flight while the
+// current one is computed; per tile, two barriers:
+//   - S^T[32 tokens x 32 heads] = K Q^T in four quarters, one per wave: wave
+//     w takes tokens 16(w & 1) .. +15 and heads 16(w >> 1) .. +15 over all
+//     576 dims on mfma_f32_16x16x32_bf16 (18 k-steps), its query slice held in
+//     registers, so no partial scores are exchanged;
+//   - each wave forms the softmax weights of its quarter against the heads'
+//     current reference maxima and writes them to LDS as bf16, with its per-
+//     head maximum and weight sum; after the barrier every wave sees the
+//     tile's maxima.  Only when a head's maximum passes its reference by
+//     more than kLazyRescale (always on the first tile) are the references
+//     raised, the weights recomputed and the running output rescaled (one
+//     more barrier);
+//   - O^T[dims x heads] += V^T P^T on mfma_f32_32x32x16_bf16: wave w owns V
+//     dims 128w .. 128w+127 (4 tiles of 32); P^T is read from LDS already in
+//     the B operand's token order; V^T is read from the K tile in LDS (so HBM
+//     sees each 576-dim row once) with the transposing 64-bit LDS read.
 //
 // Given the split scorer's scores instead of a selection (the decode step),
 // every split block first selects its request's pages itself, with the exact
-// selection of the indexer kernels, in LDS that the tile buffer takes over
+// selection of the indexer kernels, in LDS that the tile buffers take over
 // afterwards; split 0 writes the selection row.
 #include "vx_device.h"
 #include "vx_internal.h"
@@ -37,19 +42,22 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kDqk = 576, kDv = 512, kHeads = 32;
 constexpr int kPage = 64;                    // tokens per page
 constexpr int kT = 32;                       // tokens per tile
 constexpr int kRowB = kDqk * 2;              // 1152 bytes per token row
-constexpr int kLdsRow = kRowB + 32;          // padded LDS row stride
+constexpr int kLdsRow = kRowB + 16;          // padded LDS row stride (4 banks of shift per row)
+constexpr int kTileB = kT * kLdsRow;         // one tile buffer
 constexpr int kThreads = 256;
 constexpr int kChunksPerRow = kRowB / 16;    // 72
 constexpr int kLoads = kT * kChunksPerRow / kThreads;   // 9 x 16 B per thread per tile
-constexpr int kKS = kDqk / 4 / 16;           // 9 k-steps of 16 dims per wave
-constexpr int kPartStride = 20;              // floats per lane in the partial-S buffer (16 + pad)
-constexpr int kMaxPages = 256;               // pages per split (planner bound)
+constexpr int kKS = kDqk / 32;               // 18 k-steps of 32 dims (16x16x32 products)
+constexpr int kPRow = 2 * kT + 16;           // bytes per head in the weight buffer (+ pad)
+constexpr int kMaxPages = 128;               // pages per split (planner bound)
 static_assert(kT * kChunksPerRow == kLoads * kThreads, "tile copy");
-static_assert(kKS * 16 * 4 == kDqk, "k split");
+static_assert(kKS * 32 == kDqk, "k steps");
 
 __device__ __forceinline__ float neg_inf() { return -INFINITY; }
 
@@ -61,14 +69,17 @@ __host__ __device__ constexpr size_t mla_select_offset(int score_stride, int k_t
 
 template <bool SELECT>
 __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
-  __shared__ __align__(16) uint8_t ktile[kT * kLdsRow];
-  __shared__ __align__(16) float spart[4][64 * kPartStride];
+  __shared__ __align__(16) uint8_t ktile[2 * kTileB];
+  __shared__ __align__(16) uint8_t pbuf[kHeads * kPRow];   // bf16 weights, B operand order
+  __shared__ float smax[2][kHeads], ssum[2][kHeads];        // per token half and head
   __shared__ int page_phys[kMaxPages];
   __shared__ int page_logi[kMaxPages];
   __shared__ int s_count;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int hl = l & 31, hh = l >> 5;          // head (column) and k half of the 32x32 layouts
+  const int th = w & 1, hq = w >> 1;           // this wave's token half and head half of S
+  const int lr = l & 15, lg = l >> 4;          // 16x16 layouts: column and lane group
   const int split = blockIdx.x, b = blockIdx.y;
   const int G = a.H_q;                          // H_kv == 1
 
@@ -147,13 +158,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
     }
   }
 
-  // query slice as the B operand of S^T = K Q^T: head hl, dims 144w + 16ks + 8hh ..
+  // query slice as the B operand of S^T = K Q^T: head 16hq + lr, dims 32ks + 8lg ..
   bf16x8 qB[kKS];
   {
-    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.H_q + hl) * kDqk;
+    const int head = 16 * hq + lr;
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.H_q + head) * kDqk;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      const uint4 v = hl < G ? ld16(qp + 144 * w + 16 * ks + 8 * hh) : make_uint4(0, 0, 0, 0);
+      const uint4 v = head < G ? ld16(qp + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
       qB[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -164,7 +176,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float m = neg_inf(), lsum = 0.f;              // of head hl (the same in lanes hl and hl + 32)
+  // reference maxima (log2 units) of head 16hq + lr (the S layout) and of
+  // head hl (the O layout); the same values for the same head in every wave
+  float m_s = neg_inf(), m_o = neg_inf();
+  float lsum = 0.f;                              // of head hl
 
   __syncthreads();                               // page lists visible
 
@@ -184,18 +199,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
   // supplies row 4hh + j (+8, +16 s) at dims 4c .. 4c+3
   const int tr_row = 4 * hh + ((l & 15) >> 2);
   const int tr_col = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  // the weights this lane writes: S-layout head 16hq + lr, tokens 16th + 4lg ..
+  // +3, at their place in the B operand's token order (within a 16-token slice,
+  // k-half kh holds tokens 8(j/4) + 4kh + j%4, j = 0..7)
+  uint8_t* pw = pbuf + (16 * hq + lr) * kPRow + 2 * (16 * th + 8 * (lg & 1) + 4 * (lg >> 1));
 
   for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();                             // previous tile and partials consumed
+    uint8_t* kt = ktile + (t & 1) * kTileB;
+    // tile t into buffer t % 2: buffer (t - 1) % 2 may still be read (V of the
+    // previous tile), this one was last read two tiles ago, before the
+    // previous tile's second barrier
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
       const int c = tid + r * kThreads;
       const int row = c / kChunksPerRow, col = c - row * kChunksPerRow;
-      st16(ktile + row * kLdsRow + col * 16, regs[r]);
+      st16(kt + row * kLdsRow + col * 16, regs[r]);
     }
     const int j = t / (kPage / kT), half = t % (kPage / kT);
     const int tok0 = page_logi[j] * kPage + half * kT;
-    if (tok0 + kT > seq) {
+    const bool tail = tok0 + kT > seq;
+    if (tail) {
       // Rows at or past seq (the unwritten tail of the last page): their
       // scores are masked, but as V rows 0 * NaN would still reach O, so
       // each thread overwrites its own chunks of them with zeros (program
@@ -204,103 +227,96 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
       for (int r = 0; r < kLoads; ++r) {
         const int c = tid + r * kThreads;
         const int row = c / kChunksPerRow, col = c - row * kChunksPerRow;
-        if (tok0 + row >= seq) st16(ktile + row * kLdsRow + col * 16, make_uint4(0u, 0u, 0u, 0u));
+        if (tok0 + row >= seq) st16(kt + row * kLdsRow + col * 16, make_uint4(0u, 0u, 0u, 0u));
       }
     }
-    __syncthreads();
+    __syncthreads();                             // (1) tile staged
     if (t + 1 < n_tiles) load_tile(t + 1);
 
-
-    // ---- partial S^T over dims 144w .. 144w + 143
-    f32x16 sp;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sp[i] = 0.f;
+    // ---- this wave's quarter of S^T: tokens 16th + 4lg + i, head 16hq + lr
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     {
-      const uint8_t* krow = ktile + hl * kLdsRow + 2 * (144 * w + 8 * hh);
+      const uint8_t* krow = kt + (16 * th + lr) * kLdsRow + 16 * lg;
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 kA = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 32 * ks));
-        sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA, qB[ks], sp, 0, 0, 0);
+      for (int ks = 0; ks < kKS; ks += 2) {
+        const bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 64 * ks));
+        const bf16x8 k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + 64 * ks + 64));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qB[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qB[ks + 1], s1, 0, 0, 0);
       }
     }
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = s0[i] + s1[i];
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tok0 + 16 * th + 4 * lg + i >= seq) sv[i] = neg_inf();
+    }
+    // the quarter's maximum per head (16 tokens: 4 in the lane, 4 lane groups)
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     {
-      float* dst = spart[w] + l * kPartStride;
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *reinterpret_cast<float4*>(dst + 4 * v) = make_float4(sp[4 * v], sp[4 * v + 1], sp[4 * v + 2], sp[4 * v + 3]);
-    }
-    __syncthreads();
-    // whole S^T in every wave: partials added in wave order
-    float sv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float* src = spart[v] + l * kPartStride;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 x = *reinterpret_cast<const float4*>(src + 4 * q4);
-        sv[4 * q4] += x.x;
-        sv[4 * q4 + 1] += x.y;
-        sv[4 * q4 + 2] += x.z;
-        sv[4 * q4 + 3] += x.w;
-      }
-    }
-    // ---- online softmax of head hl over the tile's tokens 8(i/4) + 4hh + i%4
-    // (the scale is positive, so the maximum is taken on the unscaled scores;
-    // masking only where the tile reaches past seq, the same in every lane)
-    if (tok0 + kT > seq) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (tok0 + 8 * (i >> 2) + 4 * hh + (i & 3) >= seq) sv[i] = neg_inf();
-    }
-    float mx = sv[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-    {
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
       const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                         false, false);
       mx = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
     }
-    mx *= a.scale_log2;
-    // lazy reference: O and lsum are rescaled only when a head's maximum
-    // passes its reference by more than kLazyRescale (always on the first tile)
-    float alpha = 1.f;
-    const bool grow = __ballot(mx > m + kLazyRescale) != 0ull;
-    if (grow) {
-      const float m_new = fmaxf(m, mx);
-      alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m - m_new);
-      m = m_new;
-    }
-    const float neg_m = (m == neg_inf()) ? 0.f : -m;
-    s16x8 pk[2];
-    float ps = 0.f;
+    mx *= a.scale_log2;          // the scale is positive: the maximum of the scaled scores
+    // weights against the current reference (replaced below if it must grow)
+    auto weights = [&](float ref) {
+      const float neg_m = (ref == neg_inf()) ? 0.f : -ref;
+      float ps = 0.f;
+      s16x4 pv;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(sv[i], a.scale_log2, neg_m));
-      ps += p;
-      pk[i >> 3][i & 7] = (short)f32_to_bf16(p);
-    }
-    {
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(fmaf(sv[i], a.scale_log2, neg_m));
+        ps += p;
+        pv[i] = (short)f32_to_bf16(p);
+      }
+      *reinterpret_cast<s16x4*>(pw) = pv;
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ps), __float_as_uint(ps),
+                                                        false, false);
+      ps = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
       const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps),
                                                         false, false);
       ps = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
-    }
-    lsum = grow ? lsum * alpha + ps : lsum + ps;
-
-    // ---- O^T += V^T P^T over the tile's two 16-token slices
-    if (grow) {
+      if (lg == 0) ssum[th][16 * hq + lr] = ps;
+    };
+    weights(m_s);
+    if (lg == 0) smax[th][16 * hq + lr] = mx;
+    __syncthreads();                             // (2) weights, maxima and sums of all quarters
+    // the tile's maximum per head, in both layouts
+    const float tmax_o = fmaxf(smax[0][hl], smax[1][hl]);
+    const bool grow = __ballot(tmax_o > m_o + kLazyRescale) != 0ull;
+    float alpha = 1.f;
+    if (grow) {                                  // the same decision in every wave
+      const float tmax_s = fmaxf(smax[0][16 * hq + lr], smax[1][16 * hq + lr]);
+      const float mo_new = fmaxf(m_o, tmax_o);
+      alpha = (mo_new == neg_inf()) ? 1.f : fast_exp2(m_o - mo_new);
+      m_o = mo_new;
+      m_s = fmaxf(m_s, tmax_s);
+      weights(m_s);                              // nobody reads weights or sums before (2')
+      __syncthreads();                           // (2') weights against the new references
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
+    lsum = lsum * alpha + (ssum[0][hl] + ssum[1][hl]);
+
+    // ---- O^T += V^T P^T over the tile's two 16-token slices
+    s16x8 pk[2];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+      pk[sl] = *reinterpret_cast<const s16x8*>(pbuf + hl * kPRow + 2 * (16 * sl + 8 * hh));
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       f32x16 acc = o[dt];
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
-        const uint8_t* vsrc = ktile + (16 * sl + tr_row) * kLdsRow + 2 * (128 * w + 32 * dt + tr_col);
+        const uint8_t* vsrc = kt + (16 * sl + tr_row) * kLdsRow + 2 * (128 * w + 32 * dt + tr_col);
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(vsrc));
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -312,6 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mla_kernel(DecodeArgs a) {
       o[dt] = acc;
     }
   }
+  const float m = m_o;
 
   // ---- write: o[dt][i] is O[head hl][dim 128w + 32dt + 8(i/4) + 4hh + i%4]
   if (hl >= G) return;
