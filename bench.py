@@ -27,6 +27,7 @@ import gc
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -58,17 +59,18 @@ def _source_sha256():
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch of the fused step from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE record of this workload, or None when there is
+    """HBM bytes per step of this workload from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record (copy-calibrated), or None when there is
     none or the kernel sources changed since the counters were taken."""
-    path = os.path.join(_ROOT, "profiles", f"decode_step_{workload}_traffic.json")
+    path = os.path.join(_ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     if rec.get("source_sha256") != _source_sha256():
         return None
-    return int(rec["hbm_bytes_per_launch"])
+    w = rec.get("workloads", {}).get(workload)
+    return int(w["hbm_bytes_per_step"]) if w else None
 
 
 # ---------------------------------------------------------------- bytes
@@ -649,6 +651,75 @@ def calibrate():
     return out
 
 
+def _short_kernel(name):
+    """Kernel name without namespaces, return type and parameter list."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "", 1)
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    name = re.sub(r"\b(vx|at::native)::", "", name[:cut]).strip()
+    return name if len(name) <= 90 else name[:87] + "..."
+
+
+def summarize_trace(db_path):
+    """Markdown table of a rocprofv3 --kernel-trace results database: one row
+    per (kernel, grid, block, LDS) in first-launch order with the launch count
+    and the average / median / minimum duration."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute(
+        "select s.display_name, d.grid_size_x, d.grid_size_y, d.grid_size_z, d.workgroup_size_x,"
+        " d.group_segment_size, d.end - d.start from rocpd_kernel_dispatch d join"
+        " rocpd_info_kernel_symbol s on d.kernel_id = s.id order by d.start")
+    stats = {}
+    for name, gx, gy, gz, wg, lds, dur in rows:
+        stats.setdefault((_short_kernel(name), f"{gx // wg}x{gy}x{gz}", wg, lds), []).append(dur)
+    out = ["| kernel | grid (blocks) | block | LDS B | launches | avg us | median us | min us |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (n, g, wg, lds), d in stats.items():
+        d.sort()
+        out.append(f"| `{n}` | {g} | {wg} | {lds} | {len(d)} | {sum(d) / len(d) / 1e3:.2f} | "
+                   f"{d[len(d) // 2] / 1e3:.2f} | {d[0] / 1e3:.2f} |")
+    return "\n".join(out)
+
+
+def summarize_counters(csv_dir, pattern):
+    """Per-dispatch values of one rocprofv3 --pmc counter (csv output under
+    csv_dir) for kernels whose name matches the regular expression pattern:
+    {kernel: {"grid", "block", "dispatches", "median", "min", "max",
+    "values"}} in first-dispatch order, values in KiB as the counter reports
+    them (summed over the counter's instances per dispatch)."""
+    import csv
+    import glob
+    per = {}
+    for f in sorted(glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = _short_kernel(r["Kernel_Name"])
+                if not re.search(pattern, name):
+                    continue
+                key = (name, r.get("Grid_Size", r.get("Grid_Size_X")),
+                       r.get("Workgroup_Size", r.get("Workgroup_Size_X")))
+                d = per.setdefault(key, {})
+                did = int(r["Dispatch_Id"])
+                d[did] = d.get(did, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, grid, block), d in sorted(per.items(), key=lambda kv: min(kv[1])):
+        vals = [d[k] for k in sorted(d)]
+        srt = sorted(vals)
+        out[f"{name} grid={grid} block={block}"] = {
+            "dispatches": len(vals), "median": srt[len(srt) // 2], "min": srt[0],
+            "max": srt[-1], "values": vals if len(vals) <= 16 else None}
+    return out
+
+
 def config_entry(r):
     """One workload's line in the per-workload map."""
     d = r["dense"]
@@ -662,6 +733,7 @@ def config_entry(r):
         "dense_gbps": d["gbps"] if d else None,
         "dense_frac": d["gbps"] / HBM_PEAK_GBPS if d else None,
         "speedup_vs_dense": (d["ms_per_step"] / r["ms_per_step"]) if d else None,
+        "traffic_bytes_per_step": measured_traffic(r["w"].name),
         "steps": r["steps"],
     }
     return e
@@ -699,7 +771,19 @@ def main():
                     help="only time plain streams of known size (copies, a page gather, a "
                          "read-only sum): the streaming ceiling, and the references that "
                          "scale rocprofv3's HBM counters")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="print a markdown table of a rocprofv3 kernel-trace database and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print per-kernel values of a rocprofv3 --pmc csv run and exit")
+    ap.add_argument("--kernels", default=".",
+                    help="regular expression on kernel names for --summarize-counters")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters, args.kernels), indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library "
@@ -768,7 +852,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "vx_sparse_decode_step",
                      "achieved": r["achieved"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": r["achieved"] / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                     "traffic_unit": "HBM bytes per step (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)"},
         "cpu_baseline": cpu,
         "algorithmic_bytes_per_step": int(r["b_step"]),
