@@ -44,6 +44,9 @@ struct ScoreArgs {
   const void* k;          // [P, H_kv, S_p, D]
   void* cent_out;         // the centroid table, written
   int32_t update_completed;
+  // split scorer only: when set, a block's scores are gathered in LDS and
+  // written as whole rows at the end (set by the launcher when they fit)
+  int32_t stage_scores;
 };
 
 struct TopkArgs {

@@ -26,6 +26,8 @@
 // whole (every wave locating the boundary bin itself), then the union with
 // the reserved pages compacted in ascending page order with one block-wide
 // scan.
+#include <algorithm>
+
 #include "vx_centroid.h"
 #include "vx_select.h"
 
@@ -151,6 +153,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       sc.load(reinterpret_cast<const T*>(a.k) + (size_t)cpage * a.H_kv * a.S_p * D, a.S_p, u0, nu);
   };
   float* cred = smem + a.H_kv * D + a.cand_per_block + (NCH > 1 ? NCH * a.H_kv * D : 0);
+  // staged scores [H_kv][nc]: the completed page's reduction reuses this LDS
+  // only after the rows are written out
+  float* sst = cred;
   auto centroid_done = [&]() {
     if (!upd) return;
     sc.reduce(cred, a.S_p, nu);
@@ -190,6 +195,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const T* cent = reinterpret_cast<const T*>(a.cent);
   float* out = a.scores + (size_t)b * a.H_kv * a.score_stride;
   const int rows = nc * a.H_kv;
+  // score of candidate c0 + c for KV head h: into LDS when staging (stores of
+  // single words scattered over H_kv rows cost more than the final row copy)
+  auto put = [&](int h, int c, float v) {
+    if (LH <= 64 && a.stage_scores)
+      sst[h * nc + c] = v;
+    else
+      out[(size_t)h * a.score_stride + c0 + c] = v;
+  };
 
   if constexpr (LH <= 64) {
     // Rows r = c * H_kv + h (the H_kv rows of a page are contiguous), R per
@@ -261,7 +274,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         const int r = r0 + u * STEP;
         if (u < U && r < rows) {
           const int c = r / a.H_kv, h = r - c * a.H_kv;
-          out[(size_t)h * a.score_stride + c0 + c] = mine[j];
+          put(h, c, mine[j]);
         }
       }
     }
@@ -339,6 +352,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       if (r3 < rows) issue(r3, tb);
     }
   }
+  if (LH <= 64 && a.stage_scores) {
+    __syncthreads();
+    for (int i = tid; i < rows; i += kScoreThreads) {
+      const int h = i / nc, c = i - h * nc;
+      out[(size_t)h * a.score_stride + c0 + c] = sst[i];
+    }
+    __syncthreads();                        // sst is the centroid reduction's LDS
+  }
   centroid_done();
 }
 
@@ -389,13 +410,20 @@ size_t score_centroid_lds(int H_kv, int grid_x) {
   return (size_t)per_block * S::RG * S::E * sizeof(float);
 }
 
+// Largest staged score block (LDS): beyond it scores are stored directly.
+constexpr size_t kScoreStageBytes = 32 * 1024;
+
 template <typename T, int D>
 hipError_t run_score(const ScoreArgs& a, int grid_x, hipStream_t s) {
   const int G = a.H_q / a.H_kv, nch = (G + 7) / 8;
+  ScoreArgs b = a;
+  const size_t stage = (size_t)a.H_kv * a.cand_per_block * sizeof(float);
+  b.stage_scores = D / Vec16<T>::E <= 64 && stage <= kScoreStageBytes;
+  const size_t tail = std::max(a.update_completed ? score_centroid_lds<T, D>(a.H_kv, grid_x) : 0,
+                               b.stage_scores ? stage : 0);
   const size_t lds = (size_t)a.H_kv * D * sizeof(float) + (size_t)a.cand_per_block * sizeof(int32_t) +
-                     (nch > 1 ? (size_t)nch * a.H_kv * D * sizeof(float) : 0) +
-                     (a.update_completed ? score_centroid_lds<T, D>(a.H_kv, grid_x) : 0);
-  hipLaunchKernelGGL((score_kernel<T, D>), dim3(grid_x, a.B), dim3(kScoreThreads), lds, s, a);
+                     (nch > 1 ? (size_t)nch * a.H_kv * D * sizeof(float) : 0) + tail;
+  hipLaunchKernelGGL((score_kernel<T, D>), dim3(grid_x, a.B), dim3(kScoreThreads), lds, s, b);
   return hipGetLastError();
 }
 

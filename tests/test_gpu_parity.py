@@ -402,13 +402,14 @@ def test_decode_step_edge_lengths(vx, dtype, D, G, S, topk, bos, eos):
 
 @pytest.mark.parametrize("batch,H_kv,G,lens", [
     (80, 8, 2, (1, 15, 16, 17, 200, 513, 1600)),       # 4-wave blocks, longest first
+    (509, 8, 2, (1, 15, 16, 17, 200, 513, 1600)),      # ... more blocks than resident at once
     (520, 1, 4, (1, 16, 17, 40, 64)),                   # 4-wave blocks, request order
 ])
 def test_decode_step_many_units(vx, batch, H_kv, G, lens):
     """Two or more (request, KV head) units per CU: the fused step's 4-wave
     blocks (taken longest request first up to 512 requests, with many equal
-    lengths) write every request's row, equal to the oracle, with the same
-    selection as vx_score_topk."""
+    lengths, also with several waves of blocks) write every request's row,
+    equal to the oracle, with the same selection as vx_score_topk."""
     rng = np.random.default_rng(batch)
     seq_lens = tuple(int(x) for x in rng.choice(lens, size=batch))
     w = synth.Workload(name="many_units", batch=batch, num_q_heads=H_kv * G, num_kv_heads=H_kv,
