@@ -1,7 +1,8 @@
 """GPU parity over seeded random shapes: dtype, head dim, KV heads, group
 size, page size, batch, ragged lengths (down to one token), top-k and the
 reserved first / last page counts all drawn per case (MLA cases: batch,
-lengths, query heads, top-k and reserved pages).  Each case runs the
+lengths, query heads, top-k and reserved pages; 16 more through the
+bound-rule step).  Each case runs the
 decode step (fused or split, whichever the shape gets), the separate
 indexer, and the dense decode, and compares every request with the fp64
 oracle: selections bit for bit, outputs and lse within the usual bars, the
@@ -11,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle as orc
 import synth
 from tests import _harness as H
 
@@ -18,6 +20,7 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 64
 N_MLA_CASES = 8
+N_BOUNDS_CASES = 16
 
 
 @pytest.fixture(scope="module")
@@ -93,3 +96,54 @@ def _run(vx, w):
         _check(c, b, None, fo, fl, sparse=False)
     H.assert_centroids(c, np.concatenate([synth.setup_full_pages(c.layout),
                                           synth.completed_pages(c.layout, 0)]))
+
+
+# ------------------------------------------------------- the bound rule
+def _check_bounds_request(c, b, sel, out, lse):
+    w = c.w
+    want = H.oracle_selection(c, b, "bounds")
+    got = sel[b].cpu().numpy()
+    assert np.array_equal(got, want), f"request {b}: selected pages differ"
+    k, v = c.request_pages(b)
+    _, o_ref, lse_ref = orc.quest_decode_request(
+        c.q_host[b].double().numpy(), k, v, c.oracle_bounds(b), int(c.L[b]), w.sm_scale, w.topk,
+        w.n_bos, w.n_eos, v_dims=w.head_dim_v if v is None else None)
+    H.assert_close_out(H.to_f64(out[b]), o_ref, w.dtype, f"request {b} out")
+    H.assert_close_lse(H.to_f64(lse[b]), lse_ref, w.dtype, f"request {b}")
+
+
+@pytest.mark.parametrize("seed", range(N_BOUNDS_CASES))
+def test_random_shape_bounds(vx, seed):
+    """The bound-rule step (Quest's key bounds) over random shapes: every
+    request's selection and attention against the oracle, the selection
+    equal to vx_score_topk_bounds', the completed pages' bounds exact."""
+    w = _draw(1000 + seed)
+    H.log(f"case {H.describe(w)} B={w.batch} bos={w.n_bos} eos={w.n_eos}")
+    c = H.setup_case(vx, w)
+    bounds = torch.zeros((c.layout.num_pages, w.num_kv_heads, 2, w.head_dim_qk),
+                         dtype=w.torch_dtype, device="cuda")
+    ids = synth.setup_full_pages(c.layout)
+    if len(ids):
+        vx.bounds_update(c.kv, bounds, torch.from_numpy(ids.astype(np.int32)).cuda())
+    H.fix_gaps(c, range(w.batch), rule="bounds")
+    q = c.q_host.cuda()
+    bt = c.batch(vx)
+    sel = torch.full((w.batch, w.num_kv_heads, w.k_tot), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim_v), float("nan"), dtype=w.torch_dtype,
+                     device="cuda")
+    lse = torch.full((w.batch, w.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    vx.sparse_decode_step_bounds(c.kv, bt, bounds, q, w.topk, w.n_bos, w.n_eos, True, w.sm_scale,
+                                 sel, out, lse, vx.alloc_workspace(vx.VX_OP_DECODE_STEP, c.kv, bt,
+                                                                   w.k_tot))
+    sel_ix = torch.full_like(sel, -7)
+    vx.score_topk_bounds(c.kv, bt, bounds, q, w.topk, w.n_bos, w.n_eos, sel_ix,
+                         vx.alloc_workspace(vx.VX_OP_SCORE_TOPK, c.kv, bt))
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_ix), "the step's selection differs from vx_score_topk_bounds'"
+    for b in range(w.batch):
+        _check_bounds_request(c, b, sel, out, lse)
+    done = np.concatenate([ids, synth.completed_pages(c.layout, 0)])
+    if len(done):
+        idx = torch.from_numpy(done.astype(np.int64)).cuda()
+        assert np.array_equal(H.to_f64(bounds[idx]), orc.page_bounds(H.to_f64(c.K[idx]))), \
+            "page bounds differ"
