@@ -252,11 +252,7 @@ def alloc_workspace(op: int, kv: PagedKV, batch: Batch, k_tot: int = 0) -> torch
 
 def centroid_update(kv: PagedKV, page_ids: torch.Tensor, stream=None):
     """vx_centroid_update: centroids of the listed (full) physical pages."""
-    _need(page_ids, "page_ids", torch.int32)
-    kvs = kv.struct()
-    _check(load_library().vx_centroid_update(ctypes.byref(kvs), _ptr(page_ids),
-                                             page_ids.numel(), _stream(stream)),
-           "vx_centroid_update")
+    prepare_centroid_update(kv, page_ids, stream)()
 
 
 def append_kv(kv: PagedKV, batch: Batch, k_src: torch.Tensor, v_src: Optional[torch.Tensor],
@@ -265,20 +261,17 @@ def append_kv(kv: PagedKV, batch: Batch, k_src: torch.Tensor, v_src: Optional[to
     """vx_append_kv: request b's last n_new[b] tokens (lengths from batch,
     after the write) from rows src_start[b].. of k_src / v_src into the
     cache, with the centroids of the pages the write fills."""
+    prepare_append_kv(kv, batch, k_src, v_src, src_start, n_new, max_new, update_centroids,
+                      stream)()
+
+
+def prepare_append_kv(kv: PagedKV, batch: Batch, k_src, v_src, src_start, n_new, max_new,
+                      update_centroids=True, stream=None) -> "PreparedCall":
     _need(k_src, "k_src")
     if v_src is not None:
         _need(v_src, "v_src")
     _need(src_start, "src_start", torch.int32)
     _need(n_new, "n_new", torch.int32)
-    kvs, bs = kv.struct(), batch.struct()
-    _check(load_library().vx_append_kv(
-        ctypes.byref(kvs), ctypes.byref(bs), _ptr(k_src), _ptr(v_src), _ptr(src_start),
-        _ptr(n_new), k_src.shape[0], int(max_new), int(bool(update_centroids)),
-        _stream(stream)), "vx_append_kv")
-
-
-def prepare_append_kv(kv: PagedKV, batch: Batch, k_src, v_src, src_start, n_new, max_new,
-                      update_centroids=True, stream=None) -> "PreparedCall":
     kvs, bs = kv.struct(), batch.struct()
     lib = load_library()
     args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(k_src), _ptr(v_src), _ptr(src_start),
@@ -291,11 +284,7 @@ def prepare_append_kv(kv: PagedKV, batch: Batch, k_src, v_src, src_start, n_new,
 def score_topk(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
                n_eos: int, sel: torch.Tensor, workspace: torch.Tensor, stream=None):
     """vx_score_topk: selected logical pages per (request, KV head) into sel."""
-    _args(kv, batch, q=q, sel=sel)
-    kvs, bs = kv.struct(), batch.struct()
-    _check(load_library().vx_score_topk(
-        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, _ptr(sel),
-        _ptr(workspace), workspace.numel(), _stream(stream)), "vx_score_topk")
+    prepare_score_topk(kv, batch, q, topk, n_bos, n_eos, sel, workspace, stream)()
 
 
 def score_topk_radix(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
@@ -305,16 +294,8 @@ def score_topk_radix(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bo
     levels, then the boundary bin's members by rank from ``rnd``) into sel.
     ``rnd`` holds one random 32-bit word per (request, KV head) (int32 or
     uint32 tensor of B * H_kv elements, read as uint32)."""
-    _args(kv, batch, q=q, sel=sel)
-    if rnd.device.type != "cuda" or not rnd.is_contiguous() or rnd.element_size() != 4 or \
-            rnd.dtype.is_floating_point:
-        raise ValueError("rnd must be a contiguous 32-bit integer CUDA tensor")
-    kvs, bs = kv.struct(), batch.struct()
-    if rnd.numel() < bs.batch * kvs.num_kv_heads:
-        raise ValueError("rnd needs one word per (request, KV head)")
-    _check(load_library().vx_score_topk_radix(
-        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, levels, _ptr(rnd),
-        _ptr(sel), _ptr(workspace), workspace.numel(), _stream(stream)), "vx_score_topk_radix")
+    prepare_score_topk_radix(kv, batch, q, topk, n_bos, n_eos, levels, rnd, sel, workspace,
+                             stream)()
 
 
 def bounds_update(kv: PagedKV, bounds: torch.Tensor, page_ids: torch.Tensor, stream=None):
@@ -351,23 +332,14 @@ def sparse_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sel: torch.T
                         sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
                         workspace: torch.Tensor, stream=None):
     """vx_sparse_paged_decode: attention over the pages listed in sel."""
-    _args(kv, batch, q=q, sel=sel, out=out, lse=lse)
-    kvs, bs = kv.struct(), batch.struct()
-    _check(load_library().vx_sparse_paged_decode(
-        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), _ptr(sel), sel.shape[-1],
-        float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-        _stream(stream)), "vx_sparse_paged_decode")
+    prepare_sparse_paged_decode(kv, batch, q, sel, sm_scale, out, lse, workspace, stream)()
 
 
 def full_paged_decode(kv: PagedKV, batch: Batch, q: torch.Tensor, sm_scale: float,
                       out: torch.Tensor, lse: Optional[torch.Tensor],
                       workspace: torch.Tensor, stream=None):
     """vx_full_paged_decode: attention over every page (the dense baseline)."""
-    _args(kv, batch, q=q, out=out, lse=lse)
-    kvs, bs = kv.struct(), batch.struct()
-    _check(load_library().vx_full_paged_decode(
-        ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), float(sm_scale), _ptr(out), _ptr(lse),
-        _ptr(workspace), workspace.numel(), _stream(stream)), "vx_full_paged_decode")
+    prepare_full_paged_decode(kv, batch, q, sm_scale, out, lse, workspace, stream)()
 
 
 def sparse_decode_step(kv: PagedKV, batch: Batch, q: torch.Tensor, topk: int, n_bos: int,
@@ -472,7 +444,12 @@ def prepare_score_topk(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, sel, wo
 def prepare_score_topk_radix(kv: PagedKV, batch: Batch, q, topk, n_bos, n_eos, levels, rnd,
                              sel, workspace, stream=None) -> PreparedCall:
     _args(kv, batch, q=q, sel=sel)
+    if rnd.device.type != "cuda" or not rnd.is_contiguous() or rnd.element_size() != 4 or \
+            rnd.dtype.is_floating_point:
+        raise ValueError("rnd must be a contiguous 32-bit integer CUDA tensor")
     kvs, bs = kv.struct(), batch.struct()
+    if rnd.numel() < bs.batch * kvs.num_kv_heads:
+        raise ValueError("rnd needs one word per (request, KV head)")
     lib = load_library()
     args = (ctypes.byref(kvs), ctypes.byref(bs), _ptr(q), topk, n_bos, n_eos, levels, _ptr(rnd),
             _ptr(sel), _ptr(workspace), workspace.numel(), _stream(stream))

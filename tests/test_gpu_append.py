@@ -21,14 +21,14 @@ def vx():
     return m
 
 
-def _case(vx, dtype, D, S, lens, seed, mla=False):
+def _case(vx, dtype, D, S, lens, seed, mla=False, H_kv=2):
     if mla:
         w = synth.Workload(name="append_mla", batch=len(lens), num_q_heads=32, num_kv_heads=1,
                            head_dim_qk=576, head_dim_v=512, page_size=64, dtype="bf16", topk=4,
                            structure="mla", seed=seed, seq_lens=lens, spare_pages=3,
                            v_aliases_k=True)
     else:
-        w = synth.Workload(name="append", batch=len(lens), num_q_heads=4, num_kv_heads=2,
+        w = synth.Workload(name="append", batch=len(lens), num_q_heads=2 * H_kv, num_kv_heads=H_kv,
                            head_dim_qk=D, head_dim_v=D, page_size=S, dtype=dtype, topk=4,
                            structure="page_offset", seed=seed, seq_lens=lens, spare_pages=3)
     H.log(f"case {H.describe(w)} lens={lens}")
@@ -148,6 +148,28 @@ def test_append_mla_latent_rows(vx):
     starts = np.concatenate([[0], np.cumsum(lens2)[:-1]]).tolist()
     k_src, _ = _src(w, int(sum(lens2)), 100)
     _run_and_check(vx, c, list(lens2), starts, k_src, None, max(lens2))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_append_random_shapes(vx, seed):
+    """Seeded random writes: dtype, head dim, page size, KV heads, lengths,
+    tokens per request (none to several pages), the host bound, source rows
+    (some running past the source), with and without centroid updates."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xA99E]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    D = int(rng.choice([64, 128]))
+    S = int(rng.choice([16, 64]))
+    H_kv = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 25))
+    lens = tuple(int(x) for x in rng.integers(1, 1500, size=B))
+    n_new = [int(x) for x in rng.integers(0, 3 * S + 1, size=B)]
+    max_new = int(rng.integers(1, 3 * S + 1))
+    rows = int(sum(min(n, max_new) for n in n_new)) + 8
+    starts = [int(x) for x in rng.integers(0, rows, size=B)]
+    update = bool(rng.integers(0, 4))                       # mostly with centroids
+    w, c = _case(vx, dtype, D, S, lens, seed=500 + seed, H_kv=H_kv)
+    k_src, v_src = _src(w, rows, 600 + seed)
+    _run_and_check(vx, c, n_new, starts, k_src, v_src, max_new, update=update)
 
 
 def test_append_arguments(vx):
