@@ -29,7 +29,10 @@
  *   Ownership.  The caller owns every buffer.  The library never
  *               allocates or frees device memory and keeps no state across
  *               calls except cached device properties (compute-unit count,
- *               LDS per block); calls are reentrant.
+ *               LDS per block) and, for vx_sparse_decode_step_static only,
+ *               a static scratch array per GPU; calls are reentrant
+ *               (overlapping static-step calls on one GPU share that
+ *               scratch and race).
  *   Streams.    Work is enqueued on `stream` (NULL = the null stream);
  *               calls return after launch, never synchronise the host.
  *   Errors.     Arguments are validated on the host before any HIP call;
