@@ -264,11 +264,20 @@ def run_workload(args, name, full):
     for i in range(K_steps):
         schedule(W_steps + i)["step"]()
     ev1.record(stream)
-    enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_ms = ev0.elapsed_time(ev1)
     log(f"timed {K_steps} sparse steps: {wall * 1e3:.2f} ms wall, {region_ms:.2f} ms on the stream")
+    # host cost of one launch: a short burst from an idle queue, timed on the
+    # host before any wait (a long run blocks once the runtime's limit of
+    # launches in flight is reached, which measures the GPU instead)
+    n_host = 16
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_host):
+        schedule(i)["step"]()
+    enqueue = (time.perf_counter() - t0) * K_steps / n_host
+    torch.cuda.synchronize()
     # per-launch spread, from a second pass with events around every launch
     # (each event pair adds a few microseconds, so this pass is not the headline)
     n_ev = max(K_steps // 4, 1)
